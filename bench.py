@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the fused gate-up SwiGLU on one MI355X.
+
+A step is one pass of the hot path over one batch: the forward
+y = silu(g) * u followed by the out-of-place backward [dgate | dup], on the
+wide-FFN workload x [S=2048, B=4, 2n] with n = 32768 in bf16 (8192 tokens x
+65536 columns), inputs resident in HBM before the timed region. The value is
+algorithmic bytes per step (forward 3 and backward 5 element-sizes per
+(row, column) pair: 8 * 2 B * 8192 * 32768 = 4.295 GB) over the measured
+step time, in GB/s (1e9 B/s).
+
+Also measured in the same run: each kernel's own time from HIP events on the
+stream it runs on (forward, backward, in-place backward), a plain copy of the
+same size as the backward's traffic for context, and the CPU oracle on a
+bounded sample of the same workload (the cpu_baseline).
+
+One JSON line goes to stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused SwiGLU fwd+bwd achieved HBM GB/s (and % of peak) at S=2048,B=4,n=32768 bf16"
+PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+CALIB_BYTES = 1 << 30
+KERNEL_SRC = os.path.join(ROOT, "swiglu_activation_amd", "csrc", "swiglu_gateup.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "swiglu_bwd_wide_bf16_n32768_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per backward launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on another kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^kernel_source_sha256_16:\s*(\w+)", text, re.M)
+    t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m or not t or m.group(1) != source_digest():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, x_h, dy_h, seconds: float):
+    """The oracle as it stands, in one process, on a bounded sample of the
+    workload: consecutive 512-row blocks from row 0 until about `seconds` of
+    CPU time is spent (or the rows run out)."""
+    import oracle
+    rows = 0
+    t0 = time.perf_counter()
+    while rows < w.rows and time.perf_counter() - t0 < seconds:
+        r1 = min(rows + 512, w.rows)
+        xf = oracle.widen(x_h[rows:r1], w.dtype)
+        dyf = oracle.widen(dy_h[rows:r1], w.dtype)
+        y = oracle.oracle_fwd(xf)
+        dx = oracle.oracle_bwd(xf, dyf)
+        assert y.shape == (r1 - rows, w.n) and dx.shape == (r1 - rows, 2 * w.n)
+        rows = r1
+    dt = time.perf_counter() - t0
+    bytes_ = 8 * w.elem_bytes * rows * w.n
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"rows 0..{rows} of {w.rows} ({rows * w.n} gate/up pairs) of {w.name}: "
+                      "widen to float64, forward, backward (numpy, one thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="synthetic workload name")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time bound of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the fwd+bwd step (for profiling runs)")
+    ap.add_argument("--calib", action="store_true",
+                    help="also run plain 1 GiB copies (torch copy_ and an elementwise "
+                         "negation) as the byte-counter calibration for rocprofv3 --pmc")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported. The op is "
+              "elementwise and shards with no communication, so N GPUs each run this "
+              "single-GPU workload on their own shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import swiglu_activation_amd as sw
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    if not os.path.exists(sw.library_path()):
+        from swiglu_activation_amd import build
+        build.build()
+    sw.load_library()
+
+    w = synth.WORKLOADS[args.workload or synth.HEADLINE]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    log(f"[bench] workload {w.name}: x {w.shape} {w.dtype}; drawing inputs")
+    x_h, dy_h = synth.make_x(w), synth.make_dy(w)
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x = up(x_h).reshape(w.shape)
+    dy = up(dy_h).reshape(w.shape[:-1] + (w.n,))
+    y = torch.empty(w.shape[:-1] + (w.n,), dtype=tdt, device=dev)
+    dx = torch.empty(w.shape, dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    e = w.elem_bytes
+    pairs = w.rows * w.n
+    fwd_bytes, bwd_bytes = 3 * e * pairs, 5 * e * pairs
+    step_bytes = fwd_bytes + bwd_bytes
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        sw.swiglu_gateup_fwd(x, y)
+        sw.swiglu_gateup_bwd(dy, x, dx)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        sw.swiglu_gateup_fwd(x, y)
+        ev[k][1].record(stream)
+        sw.swiglu_gateup_bwd(dy, x, dx)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
+    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]
+    fwd_avg, bwd_avg = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step:.4f} ms -> {value:.1f} GB/s; fwd {fwd_avg:.4f} ms, "
+        f"bwd {bwd_avg:.4f} ms")
+
+    passes = {
+        "fwd": {"ms_avg": round(fwd_avg, 5), "ms_min": round(min(fwd_ms), 5),
+                "GBps": round(fwd_bytes / fwd_avg / 1e6, 1), "bytes": fwd_bytes},
+        "bwd": {"ms_avg": round(bwd_avg, 5), "ms_min": round(min(bwd_ms), 5),
+                "GBps": round(bwd_bytes / bwd_avg / 1e6, 1), "bytes": bwd_bytes},
+        "fwd+bwd_kernels": {"ms_avg": round(fwd_avg + bwd_avg, 5),
+                            "GBps": round(step_bytes / (fwd_avg + bwd_avg) / 1e6, 1)},
+    }
+
+    if not args.no_extras:
+        # In-place backward: each timed launch overwrites a fresh copy of x,
+        # restored outside the timed events.
+        x0 = x.detach().clone()
+        ip_ms = []
+        for k in range(max(5, K // 2) + 2):
+            x.copy_(x0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sw.swiglu_gateup_bwd(dy, x, in_place=True)
+            b.record(stream)
+            b.synchronize()
+            if k >= 2:
+                ip_ms.append(a.elapsed_time(b))
+        x.copy_(x0)
+        del x0
+        ip_avg = float(np.mean(ip_ms))
+        passes["bwd_in_place"] = {"ms_avg": round(ip_avg, 5), "ms_min": round(min(ip_ms), 5),
+                                  "GBps": round(bwd_bytes / ip_avg / 1e6, 1), "bytes": bwd_bytes}
+        # A plain copy moving the backward's byte count (read half, write half)
+        # as the empirical streaming ceiling, for context.
+        nbytes = bwd_bytes // 2
+        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        cms = []
+        for k in range(12):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            b.synchronize()
+            if k >= 2:
+                cms.append(a.elapsed_time(b))
+        cavg = float(np.mean(cms))
+        passes["copy_same_bytes"] = {"ms_avg": round(cavg, 5),
+                                     "GBps": round(2 * nbytes / cavg / 1e6, 1),
+                                     "bytes": 2 * nbytes, "kind": "torch copy_ (context)"}
+        del src, dst
+        log(f"[bench] bwd in_place {ip_avg:.4f} ms; copy {cavg:.4f} ms")
+
+    if args.calib:
+        # Known-size plain copies: each reads and writes exactly CALIB_BYTES.
+        src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copies of {CALIB_BYTES} bytes done")
+
+    achieved = bwd_bytes / (bwd_avg * 1e-3) / 1e9
+    traffic = read_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.rows, "S": w.shape[0] if len(w.shape) == 3 else None,
+                   "B": w.shape[1] if len(w.shape) == 3 else None, "n": w.n,
+                   "x_shape": list(w.shape), "step": "forward + out-of-place backward",
+                   "bytes_per_step": step_bytes},
+        "pct_of_peak": round(100.0 * value / PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "swiglu_bwd_kernel (out of place)",
+                     "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "passes": passes,
+        "kernel_source_sha256_16": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle for about {args.cpu_seconds} s")
+        out["cpu_baseline"] = cpu_baseline(w, x_h, dy_h, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

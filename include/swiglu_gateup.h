@@ -1,0 +1,125 @@
+/*
+ * swiglu_gateup.h -- C ABI of the fused gate-up SwiGLU for AMD MI355X (gfx950).
+ *
+ * The operation (Liger-Kernel Megatron SwiGLU page, §Background and
+ * §What's added): the fc1 projection of a Megatron-style MLP produces ONE
+ * packed tensor x of shape [rows, 2n] -- rows are the flattened leading
+ * dimensions (tokens, or sequence x batch), the gate half g is columns [0, n)
+ * and the up half u is columns [n, 2n). The fused forward reads both halves of
+ * each row through a column offset, with no split, copy or concatenation, and
+ * writes y = silu(g) * u of shape [rows, n]; silu(z) = z * sigma(z),
+ * sigma(z) = 1 / (1 + exp(-z)). The backward recomputes silu from the saved x
+ * and writes dx = [dgate | dup] of shape [rows, 2n] with
+ *     dgate = dy * u * sigma(g) * (1 + g * (1 - sigma(g)))
+ *     dup   = dy * silu(g)
+ * either into a separate buffer or, in place, over x (same page, §Optional
+ * in_place). Supported element types are fp32 and bf16 (same page, §Megatron
+ * feature compatibility). All arithmetic is fp32 in registers; bf16 results
+ * are rounded once, to nearest even.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers on the current HIP device. The caller owns
+ *    every buffer; the library allocates nothing, frees nothing, keeps no
+ *    per-call state, and never synchronizes.
+ *  - Row strides are counted in ELEMENTS (not bytes); columns are contiguous
+ *    (unit stride). A row stride larger than the row's width is allowed (for
+ *    example a view into a wider buffer); the columns past the width are never
+ *    read or written.
+ *  - Work is enqueued on `stream` (0 = the null stream) and runs
+ *    asynchronously; a return of SWIGLU_OK means "validated and launched".
+ *  - Every argument check happens on the host before anything is launched. On
+ *    an error nothing is written and no HIP call is made.
+ *  - rows == 0 or n == 0 is a valid empty problem: SWIGLU_OK, no launch.
+ *  - Pointer alignment is never an error: 16-byte vector loads and stores are
+ *    used when the base pointers, n and the row strides allow them, narrower
+ *    accesses otherwise.
+ *  - Results are bitwise deterministic, and the in-place backward produces the
+ *    same bits as the out-of-place one.
+ *  - Two calls that write the same memory must not run concurrently.
+ */
+#ifndef SWIGLU_GATEUP_H
+#define SWIGLU_GATEUP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of x, y, dy and dx (all four share it). */
+typedef enum {
+    SWIGLU_DTYPE_F32 = 0,   /* IEEE binary32 */
+    SWIGLU_DTYPE_BF16 = 1   /* bfloat16: 1 sign, 8 exponent, 7 mantissa bits */
+} swiglu_dtype;
+
+typedef enum {
+    SWIGLU_OK = 0,
+    SWIGLU_ERR_NULL_POINTER = 1,  /* a required pointer is NULL (and the problem is not empty) */
+    SWIGLU_ERR_BAD_SHAPE = 2,     /* rows < 0, n < 0, or 2n / rows*stride overflow int64 */
+    SWIGLU_ERR_BAD_STRIDE = 3,    /* a row stride is smaller than its row's width */
+    SWIGLU_ERR_BAD_DTYPE = 4,     /* dtype is neither SWIGLU_DTYPE_F32 nor SWIGLU_DTYPE_BF16 */
+    SWIGLU_ERR_ALIASING = 5,      /* outputs overlap inputs where that is not allowed */
+    SWIGLU_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed */
+} swiglu_status;
+
+/*
+ * Forward (Liger-Kernel Megatron SwiGLU page, §Background: input row stride
+ * 2n, output row stride n).
+ *
+ *   x            [rows, 2n] input, read only; row r starts at x + r*x_row_stride.
+ *   x_row_stride elements between rows of x; must be >= 2n.
+ *   y            [rows, n] output; row r starts at y + r*y_row_stride.
+ *   y_row_stride elements between rows of y; must be >= n.
+ *   rows, n      problem size; >= 0.
+ *   dtype        element type of x and y.
+ *   stream       HIP stream the kernel is enqueued on.
+ *
+ * Errors: SWIGLU_ERR_NULL_POINTER (x or y NULL), SWIGLU_ERR_BAD_SHAPE,
+ * SWIGLU_ERR_BAD_STRIDE, SWIGLU_ERR_BAD_DTYPE, SWIGLU_ERR_ALIASING (the
+ * memory span of y overlaps that of x), SWIGLU_ERR_HIP (launch failed).
+ */
+swiglu_status swiglu_gateup_fwd(const void* x, int64_t x_row_stride,
+                                void* y, int64_t y_row_stride,
+                                int64_t rows, int64_t n,
+                                swiglu_dtype dtype, hipStream_t stream);
+
+/*
+ * Backward (same page, §What's added: a backward kernel over the [tokens, 2n]
+ * layout; §Optional in_place: the gradient may overwrite the fc1 output).
+ *
+ *   dy            [rows, n] upstream gradient, read only.
+ *   dy_row_stride elements between rows of dy; must be >= n.
+ *   x             [rows, 2n] saved forward input. Read only when in_place == 0;
+ *                 when in_place != 0 it is read and then overwritten, element
+ *                 by element, with dx = [dgate | dup].
+ *   x_row_stride  elements between rows of x; must be >= 2n.
+ *   dx            out of place: [rows, 2n] output buffer, must not overlap x
+ *                 or dy. In place: must be NULL or equal to x (x is then the
+ *                 output).
+ *   dx_row_stride out of place: elements between rows of dx, >= 2n. In place:
+ *                 ignored (x_row_stride is used).
+ *   rows, n       problem size; >= 0.
+ *   dtype         element type of dy, x and dx.
+ *   in_place      0 = write dx; nonzero = overwrite x.
+ *   stream        HIP stream the kernel is enqueued on.
+ *
+ * Errors: SWIGLU_ERR_NULL_POINTER (dy or x NULL, or dx NULL out of place),
+ * SWIGLU_ERR_BAD_SHAPE, SWIGLU_ERR_BAD_STRIDE, SWIGLU_ERR_BAD_DTYPE,
+ * SWIGLU_ERR_ALIASING (out of place: dx overlaps x or dy; in place: dx is
+ * neither NULL nor x, or dy overlaps x), SWIGLU_ERR_HIP (launch failed).
+ */
+swiglu_status swiglu_gateup_bwd(const void* dy, int64_t dy_row_stride,
+                                void* x, int64_t x_row_stride,
+                                void* dx, int64_t dx_row_stride,
+                                int64_t rows, int64_t n,
+                                swiglu_dtype dtype, int in_place, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* swiglu_status_string(swiglu_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_GATEUP_H */

@@ -1,0 +1,212 @@
+"""Fused gate-up SwiGLU for AMD MI355X: Python binding of libswiglu_gateup.so.
+
+The binding only marshals arguments: it flattens leading dimensions into rows,
+reads row strides, allocates outputs with torch, and passes device pointers
+and torch's current HIP stream to the C ABI (include/swiglu_gateup.h). Every
+step of the computation runs in the HIP kernels. There is no fallback: if the
+library is missing or cannot be loaded, every call raises.
+
+Layout (Liger-Kernel Megatron SwiGLU page, §Background): x is the packed fc1
+output [..., 2n] with the gate in [..., :n] and up in [..., n:]; 2D and 3D
+inputs are accepted (§Megatron feature compatibility).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_status_string",
+           "SwiGLUError", "library_path", "load_library", "EXPORTS"]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "libswiglu_gateup.so")
+
+# Status codes and dtype codes of include/swiglu_gateup.h.
+SWIGLU_OK = 0
+SWIGLU_ERR_NULL_POINTER = 1
+SWIGLU_ERR_BAD_SHAPE = 2
+SWIGLU_ERR_BAD_STRIDE = 3
+SWIGLU_ERR_BAD_DTYPE = 4
+SWIGLU_ERR_ALIASING = 5
+SWIGLU_ERR_HIP = 6
+SWIGLU_DTYPE_F32 = 0
+SWIGLU_DTYPE_BF16 = 1
+_BAD_DTYPE_CODE = -1    # passed for any other torch dtype; the library rejects it
+
+EXPORTS = ("swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_status_string")
+
+_lib = None
+
+
+class SwiGLUError(RuntimeError):
+    """A nonzero swiglu_status from the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {swiglu_status_string(status)}")
+
+
+class SwiGLUArgumentError(SwiGLUError, ValueError):
+    """The library rejected the arguments (nothing was launched)."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libswiglu_gateup.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m swiglu_activation_amd.build` "
+            "(or __graft_entry__.build()) first. There is no non-HIP fallback.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, cint = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.swiglu_gateup_fwd.argtypes = [vp, i64, vp, i64, i64, i64, cint, vp]
+    lib.swiglu_gateup_fwd.restype = cint
+    lib.swiglu_gateup_bwd.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, cint, cint, vp]
+    lib.swiglu_gateup_bwd.restype = cint
+    lib.swiglu_status_string.argtypes = [cint]
+    lib.swiglu_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def swiglu_status_string(status: int) -> str:
+    return load_library().swiglu_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status == SWIGLU_OK:
+        return
+    if status == SWIGLU_ERR_HIP:
+        raise SwiGLUError(status, what)
+    raise SwiGLUArgumentError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# Tensor marshalling
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SWIGLU_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SWIGLU_DTYPE_BF16
+    return _BAD_DTYPE_CODE
+
+
+def _rows_and_stride(t, name: str):
+    """View t as [rows, width] with unit column stride: (rows, row_stride)."""
+    if t.dim() < 1:
+        raise ValueError(f"{name} must have at least one dimension")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+    rows = 1
+    for s in t.shape[:-1]:
+        rows *= int(s)
+    if t.dim() == 1:
+        return rows, int(t.shape[-1])
+    # leading dims must collapse into one row index with a single stride
+    row_stride = None
+    expect = None
+    for d in range(t.dim() - 2, -1, -1):
+        if t.shape[d] == 1:
+            continue
+        if row_stride is None:
+            row_stride = int(t.stride(d))
+            expect = row_stride * int(t.shape[d])
+        else:
+            if int(t.stride(d)) != expect:
+                raise ValueError(f"leading dimensions of {name} do not collapse into rows")
+            expect = int(t.stride(d)) * int(t.shape[d])
+    if row_stride is None:          # a single row
+        row_stride = int(t.shape[-1])
+    return rows, row_stride
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device (device pointers only)")
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError("all tensors must be on the same device")
+
+
+def _stream_handle(device, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def swiglu_gateup_fwd(x, y=None, *, stream=None):
+    """y = silu(x[..., :n]) * x[..., n:] for x of shape [..., 2n] (fp32 or bf16).
+
+    ``y`` (optional) is the [..., n] output; allocated when omitted. The
+    kernel is enqueued on ``stream`` (default: torch's current stream)."""
+    import torch
+    lib = load_library()
+    _require_device(x, y)
+    if x.dim() < 1 or x.shape[-1] % 2:
+        raise ValueError("last dimension of x must be even (2n)")
+    n = x.shape[-1] // 2
+    if y is None:
+        y = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    if y.dtype != x.dtype:
+        raise ValueError("x and y must have the same dtype")
+    rows, xs = _rows_and_stride(x, "x")
+    yrows, ys = _rows_and_stride(y, "y")
+    if yrows != rows or y.shape[-1] != n:
+        raise ValueError(f"y must hold {rows} rows of {n} elements")
+    with torch.cuda.device(x.device):
+        st = lib.swiglu_gateup_fwd(x.data_ptr(), xs, y.data_ptr(), ys, rows, n,
+                                   _dtype_code(x), _stream_handle(x.device, stream))
+    _check(st, "swiglu_gateup_fwd")
+    return y
+
+
+def swiglu_gateup_bwd(dy, x, dx=None, *, in_place: bool = False, stream=None):
+    """Gradient of swiglu_gateup_fwd with respect to x: [dgate | dup], [..., 2n].
+
+    silu is recomputed from the saved input ``x``. Out of place (default) the
+    result goes to ``dx`` (allocated when omitted). With ``in_place=True`` it
+    overwrites ``x``, which is returned."""
+    import torch
+    lib = load_library()
+    _require_device(dy, x, dx)
+    if x.dim() < 1 or x.shape[-1] % 2:
+        raise ValueError("last dimension of x must be even (2n)")
+    n = x.shape[-1] // 2
+    if dy.dtype != x.dtype:
+        raise ValueError("dy and x must have the same dtype")
+    rows, xs = _rows_and_stride(x, "x")
+    dyrows, dys = _rows_and_stride(dy, "dy")
+    if dyrows != rows or dy.shape[-1] != n:
+        raise ValueError(f"dy must hold {rows} rows of {n} elements")
+    if in_place:
+        if dx is not None and dx.data_ptr() != x.data_ptr():
+            raise ValueError("in_place backward writes into x; pass dx=None or dx=x")
+        dx_ptr, dxs = None, 0
+        out = x
+    else:
+        if dx is None:
+            dx = torch.empty(tuple(x.shape), dtype=x.dtype, device=x.device)
+        if dx.dtype != x.dtype:
+            raise ValueError("dx and x must have the same dtype")
+        dxrows, dxs = _rows_and_stride(dx, "dx")
+        if dxrows != rows or dx.shape[-1] != 2 * n:
+            raise ValueError(f"dx must hold {rows} rows of {2 * n} elements")
+        dx_ptr = dx.data_ptr()
+        out = dx
+    with torch.cuda.device(x.device):
+        st = lib.swiglu_gateup_bwd(dy.data_ptr(), dys, x.data_ptr(), xs, dx_ptr, dxs, rows, n,
+                                   _dtype_code(x), 1 if in_place else 0,
+                                   _stream_handle(x.device, stream))
+    _check(st, "swiglu_gateup_bwd")
+    return out

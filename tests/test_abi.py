@@ -1,0 +1,177 @@
+"""The C-ABI library on the host: it loads, exports what the header declares,
+and rejects bad arguments before any HIP call (no GPU needed; no call here
+passes validation, so nothing is ever launched)."""
+
+from __future__ import annotations
+
+import ctypes
+import glob
+import math
+import os
+import re
+import subprocess
+
+import mpmath
+import numpy as np
+import pytest
+
+import swiglu_activation_amd as sw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_visible() -> bool:
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sw.library_path()):
+        from swiglu_activation_amd import build
+        build.build()
+    return sw.load_library()
+
+
+def _declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(sw.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sw.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = sw.swiglu_status_string(code)
+        assert s.startswith("SWIGLU_")
+    assert "UNKNOWN" in sw.swiglu_status_string(99)
+
+
+# Fake, never-dereferenced addresses: every call below must fail validation.
+# They are only passed where no GPU is reachable, so a test mistake that let
+# one through could not launch a kernel on them.
+A, B, C = 0x100000, 0x900000, 0x1100000
+
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses are only "
+                                 "passed to the library on hosts without a GPU")
+F32, BF16 = sw.SWIGLU_DTYPE_F32, sw.SWIGLU_DTYPE_BF16
+
+
+def fwd(lib, x, xs, y, ys, rows, n, dt=BF16):
+    return lib.swiglu_gateup_fwd(x, xs, y, ys, rows, n, dt, None)
+
+
+def bwd(lib, dy, dys, x, xs, dx, dxs, rows, n, dt=BF16, ip=0):
+    return lib.swiglu_gateup_bwd(dy, dys, x, xs, dx, dxs, rows, n, dt, ip, None)
+
+
+@no_gpu_only
+def test_fwd_validation(lib):
+    assert fwd(lib, A, 16, B, 8, 4, 8, dt=7) == sw.SWIGLU_ERR_BAD_DTYPE
+    assert fwd(lib, A, 16, B, 8, 4, 8, dt=-1) == sw.SWIGLU_ERR_BAD_DTYPE
+    assert fwd(lib, A, 16, B, 8, -1, 8) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert fwd(lib, A, 16, B, 8, 4, -8) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert fwd(lib, A, 2 ** 33, B, 2 ** 32, 4, 2 ** 31) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert fwd(lib, A, 15, B, 8, 4, 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert fwd(lib, A, 16, B, 7, 4, 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert fwd(lib, A, 2 ** 40, B, 8, 2 ** 40, 8) == sw.SWIGLU_ERR_BAD_SHAPE   # byte span overflows
+    assert fwd(lib, None, 16, B, 8, 4, 8) == sw.SWIGLU_ERR_NULL_POINTER
+    assert fwd(lib, A, 16, None, 8, 4, 8) == sw.SWIGLU_ERR_NULL_POINTER
+    # y overlaps x: x spans [A, A + (3*16+16)*2) bytes
+    assert fwd(lib, A, 16, A + 64, 8, 4, 8) == sw.SWIGLU_ERR_ALIASING
+    assert fwd(lib, A + 32, 16, A, 8, 4, 8) == sw.SWIGLU_ERR_ALIASING   # y spans [A, A+64)
+    assert fwd(lib, A, 16, A, 8, 4, 8, dt=F32) == sw.SWIGLU_ERR_ALIASING
+
+
+@no_gpu_only
+def test_empty_problems_launch_nothing(lib):
+    # No HIP call is made for an empty problem, so these succeed without a GPU.
+    assert fwd(lib, None, 16, None, 8, 0, 8) == sw.SWIGLU_OK
+    assert fwd(lib, None, 0, None, 0, 5, 0) == sw.SWIGLU_OK
+    assert bwd(lib, None, 8, None, 16, None, 16, 0, 8) == sw.SWIGLU_OK
+    assert bwd(lib, None, 0, None, 0, None, 0, 3, 0, ip=1) == sw.SWIGLU_OK
+
+
+@no_gpu_only
+def test_bwd_validation(lib):
+    assert bwd(lib, A, 8, B, 16, C, 16, 4, 8, dt=3) == sw.SWIGLU_ERR_BAD_DTYPE
+    assert bwd(lib, A, 8, B, 16, C, 16, -2, 8) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert bwd(lib, A, 7, B, 16, C, 16, 4, 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert bwd(lib, A, 8, B, 15, C, 16, 4, 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert bwd(lib, A, 8, B, 16, C, 15, 4, 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert bwd(lib, None, 8, B, 16, C, 16, 4, 8) == sw.SWIGLU_ERR_NULL_POINTER
+    assert bwd(lib, A, 8, None, 16, C, 16, 4, 8) == sw.SWIGLU_ERR_NULL_POINTER
+    assert bwd(lib, A, 8, B, 16, None, 16, 4, 8) == sw.SWIGLU_ERR_NULL_POINTER
+    # out of place: dx must not overlap x or dy
+    assert bwd(lib, A, 8, B, 16, B + 32, 16, 4, 8) == sw.SWIGLU_ERR_ALIASING
+    assert bwd(lib, A, 8, B, 16, A, 16, 4, 8) == sw.SWIGLU_ERR_ALIASING
+    # in place: dx must be NULL or x, and dy must not overlap x
+    assert bwd(lib, A, 8, B, 16, C, 16, 4, 8, ip=1) == sw.SWIGLU_ERR_ALIASING
+    assert bwd(lib, B + 16, 8, B, 16, None, 0, 4, 8, ip=1) == sw.SWIGLU_ERR_ALIASING
+    assert bwd(lib, A, 8, B, 15, None, 0, 4, 8, ip=1) == sw.SWIGLU_ERR_BAD_STRIDE
+    # in place ignores dx_row_stride (x's is used), so a bad one is not an error
+    # by itself; this call still fails, on the NULL x.
+    assert bwd(lib, A, 8, None, 16, None, 3, 4, 8, ip=1) == sw.SWIGLU_ERR_NULL_POINTER
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 16)
+    with pytest.raises(ValueError):
+        sw.swiglu_gateup_fwd(x)
+    with pytest.raises(ValueError):
+        sw.swiglu_gateup_bwd(torch.zeros(4, 8), x)
+
+
+def test_row_flattening():
+    import torch
+    t = torch.zeros(3, 5, 16)
+    assert sw._rows_and_stride(t, "t") == (15, 16)
+    wide = torch.zeros(6, 40)[:, :16]
+    assert sw._rows_and_stride(wide, "t") == (6, 40)
+    assert sw._rows_and_stride(torch.zeros(1, 1, 16), "t") == (1, 16)
+    with pytest.raises(ValueError):
+        sw._rows_and_stride(torch.zeros(4, 6, 16).transpose(0, 1), "t")
+    with pytest.raises(ValueError):
+        sw._rows_and_stride(torch.zeros(16, 4).t(), "t")
+
+
+def _hex_const(src: str, name: str) -> float:
+    m = re.search(rf"constexpr float {name} = (-?0x[0-9a-fA-Fp.+-]+)f;", src)
+    assert m, name
+    return float.fromhex(m.group(1))
+
+
+def test_kernel_constants_match_their_definitions():
+    """The fp32 constants in the kernel source equal the splits of log2(e),
+    ln 2, g0 = -1 - W(1/e) and e^{g0}, derived here at 50 digits."""
+    src = open(os.path.join(ROOT, "swiglu_activation_amd", "csrc", "swiglu_gateup.hip")).read()
+    with mpmath.workdps(50):
+        l2e = 1 / mpmath.log(2)
+        g0 = -1 - mpmath.lambertw(1 / mpmath.e).real
+
+        def split(v):
+            hi = float(np.float32(float(v)))
+            lo = float(np.float32(float(v - mpmath.mpf(hi))))
+            return hi, lo
+
+        assert (_hex_const(src, "kLog2eHi"), _hex_const(src, "kLog2eLo")) == split(l2e)
+        assert _hex_const(src, "kLn2") == float(np.float32(float(mpmath.log(2))))
+        assert (_hex_const(src, "kG0Hi"), _hex_const(src, "kG0Lo")) == split(g0)
+        assert _hex_const(src, "kC") == float(np.float32(float(mpmath.exp(g0))))
+        assert abs(float(mpmath.exp(g0) + 1 + g0)) < 1e-40
