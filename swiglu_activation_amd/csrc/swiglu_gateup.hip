@@ -8,43 +8,43 @@
 // silu from x and write dgate = dy * u * sigma(g) * (1 + g (1 - sigma(g))) and
 // dup = dy * silu(g), to a separate [rows, 2n] buffer or over x.
 //
-// Design: the op is elementwise and streams every byte exactly once, so it is
-// bound by HBM bandwidth, not by MFMA or LDS (there is no reuse to stage).
-// Each lane owns 16-byte vectors (8 bf16 or 4 fp32 elements) and keeps
-// UNROLL of them in flight per stream before touching any result; the
-// (row, vector) space is flattened so narrow rows leave no idle lanes; the
-// grid is a fixed multiple of the CU count and strides over that space.
-// All arithmetic is fp32 in registers; bf16 results are rounded once,
-// nearest-even, by the hardware convert.
+// Design. The op is elementwise and touches every byte once, so there is no
+// reuse for LDS or MFMA to exploit; the kernels are HBM streams.
+//  * Each lane owns ONE vector (16 bytes when alignment allows: 8 bf16 or 4
+//    fp32 elements) of every stream: it loads the gate, up (and dy) vectors,
+//    computes in fp32 registers and stores the result vectors. Consecutive
+//    lanes own consecutive vectors, so each wave64 load or store covers 1 KiB
+//    of contiguous memory.
+//  * The grid is one-shot and 2D: blockIdx.y picks a row (or, for rows
+//    narrower than a block, a group of rows), blockIdx.x a 256-vector column
+//    tile. Row offsets are uniform per block and live in scalar registers; no
+//    lane divides. Enough blocks are in flight that HBM stays saturated
+//    (131072 blocks for 8192 x 32768 bf16).
+//  * Loads and stores carry the nontemporal hint: nothing is re-read, and
+//    keeping the stream out of the caches measured faster on large shapes.
+//  * Arithmetic is kept short because at 16 bytes per lane the forward has
+//    only ~29 VALU slots per element pair at 8 TB/s: bf16 uses one exp2 and
+//    one reciprocal per element with no selects; fp32 (half the elements per
+//    lane, same bytes) affords a compensated exponential and a series at the
+//    root of silu' for its tighter tolerance. bf16 results are rounded once,
+//    nearest-even, by the hardware convert.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 
 #include "swiglu_gateup.h"
 
-#ifndef SWIGLU_BLOCK
-#define SWIGLU_BLOCK 256        // threads per workgroup (4 wave64)
-#endif
-#ifndef SWIGLU_UNROLL
-#define SWIGLU_UNROLL 4         // 16-byte vectors in flight per lane and stream
-#endif
-#ifndef SWIGLU_BLOCKS_PER_CU
-#define SWIGLU_BLOCKS_PER_CU 8  // grid cap = CUs * this
-#endif
 #ifndef SWIGLU_NT_LOAD
-#define SWIGLU_NT_LOAD 0        // nontemporal hint on loads
+#define SWIGLU_NT_LOAD 1        // nontemporal hint on loads
 #endif
 #ifndef SWIGLU_NT_STORE
-#define SWIGLU_NT_STORE 0       // nontemporal hint on stores
-#endif
-#ifndef SWIGLU_ROOT_SERIES_BF16
-#define SWIGLU_ROOT_SERIES_BF16 1   // also use the root series for bf16
+#define SWIGLU_NT_STORE 1       // nontemporal hint on stores
 #endif
 
 namespace {
 
-constexpr int kBlock = SWIGLU_BLOCK;
-constexpr int kUnroll = SWIGLU_UNROLL;
+constexpr int kBlock = 256;                 // threads (4 wave64) and vectors per tile
+constexpr uint32_t kMaxGridY = 65535;       // row groups per launch; more rows -> more launches
 
 // ---------------------------------------------------------------------------
 // Element access: VEC elements of T as one load/store of VEC*sizeof(T) bytes.
@@ -84,7 +84,7 @@ struct Vec {
     static constexpr int kBytes = VEC * (int)sizeof(T);
     typedef typename Raw<kBytes>::type R;
 
-    // Load VEC elements starting at p and widen them to fp32.
+    // Load VEC elements starting at p and widen them to fp32 (exact).
     static __device__ __forceinline__ void load(const T* p, float (&f)[VEC]) {
         R r = load_raw<R>(p);
         if constexpr (sizeof(T) == 4) {
@@ -136,10 +136,32 @@ constexpr float kG0Hi = -0x1.474974p+0f;
 constexpr float kG0Lo = 0x1.bdf6fap-27f;
 constexpr float kC = 0x1.1d25d0p-2f;        // e^{g0} = -(1 + g0)
 
+// --- bf16 path: sigma with one exp2 and one reciprocal -----------------------
+// With E = e^{-g} 2^-64 and r = 1 / (2^-64 + E):
+//   sigma(g) = r 2^-64   and   1 - sigma(g) = e^{-g} sigma(g) = E r.
+// The 2^-64 shift keeps E finite for g >= -131 and r a normal number, so
+// the hardware exp2 and reciprocal (which do not produce subnormals) are
+// never asked for one; the final multiply by 2^-64 rounds correctly into the
+// subnormal range. Below g = -131.7, E overflows to inf and r is 0, which is
+// sigma(g) there to fp32 precision; 1 - sigma = E r would then be inf * 0,
+// so when it is wanted (WANT_OSIG) the exponent is clamped to 126 instead,
+// giving r = 2^-126 and E r = 1. Relative error of sigma is a few 1e-6: far
+// inside one bf16 step (2^-8).
+template <bool WANT_OSIG>
+__device__ __forceinline__ void sigmoid_fast(float g, float& sig, float& osig) {
+    float a = __builtin_fmaf(-g, kLog2eHi, -64.0f);
+    if constexpr (WANT_OSIG) a = __builtin_fminf(a, 126.0f);
+    const float E = __builtin_amdgcn_exp2f(a);
+    const float r = __builtin_amdgcn_rcpf(0x1p-64f + E);
+    sig = r * 0x1p-64f;
+    if constexpr (WANT_OSIG) osig = E * r;
+}
+
+// --- fp32 path: compensated exponential ---------------------------------------
 // e^{-a} for a >= 0 (a = +inf gives 0, a NaN gives NaN). Written as
 // 2^{-a log2 e}: the product is split so the exponent keeps ~48 bits, the
-// hardware 2^x (v_exp_f32) does the rest, and the tail of the exponent is
-// applied as a first-order correction. v_exp_f32 does not return subnormal
+// hardware 2^x does the rest, and the tail of the exponent is applied as a
+// first-order correction. The hardware 2^x does not return subnormal
 // results, so arguments below -126 are lifted by 64 and scaled back by an
 // exact multiply, which rounds correctly into the subnormal range.
 __device__ __forceinline__ float exp_neg(float a) {
@@ -157,7 +179,7 @@ __device__ __forceinline__ float exp_neg(float a) {
 // sigma(g) and 1 - sigma(g) without cancellation and without forming inf:
 // with e = e^{-|g|} and d = 1/(1+e) = sigma(|g|), sigma(g) is d for g >= 0 and
 // e*d otherwise, and 1 - sigma(g) = sigma(-g) is the other one.
-__device__ __forceinline__ void sigmoid_pair(float g, float& sig, float& osig) {
+__device__ __forceinline__ void sigmoid_accurate(float g, float& sig, float& osig) {
     const float e = exp_neg(__builtin_fabsf(g));
     const float d = __builtin_amdgcn_rcpf(1.0f + e);
     const float ed = e * d;
@@ -173,201 +195,119 @@ __device__ __forceinline__ void sigmoid_pair(float g, float& sig, float& osig) {
 // bracket in t has no cancellation: t (1 + c) + c (t^2/2! + t^3/3! + ...).
 // It is used for |t| < 1/4 (series truncated after t^7: relative error below
 // 1e-9); the direct form elsewhere, where |h| > 0.24.
-template <bool ROOT_SERIES>
-__device__ __forceinline__ float h_factor(float g, float osig) {
+__device__ __forceinline__ float h_root_series(float g, float osig) {
     const float direct = __builtin_fmaf(g, osig, 1.0f);
-    if constexpr (!ROOT_SERIES) {
-        return direct;
-    } else {
-        const float t = (g - kG0Hi) - kG0Lo;   // g - kG0Hi is exact near g0
-        float q = kC * (1.0f / 5040.0f);
-        q = __builtin_fmaf(q, t, kC * (1.0f / 720.0f));
-        q = __builtin_fmaf(q, t, kC * (1.0f / 120.0f));
-        q = __builtin_fmaf(q, t, kC * (1.0f / 24.0f));
-        q = __builtin_fmaf(q, t, kC * (1.0f / 6.0f));
-        q = __builtin_fmaf(q, t, kC * 0.5f);
-        q = __builtin_fmaf(q, t, 1.0f + kC);
-        const float series = (q * t) * osig;
-        return __builtin_fabsf(t) < 0.25f ? series : direct;
-    }
+    const float t = (g - kG0Hi) - kG0Lo;   // g - kG0Hi is exact near g0
+    float q = kC * (1.0f / 5040.0f);
+    q = __builtin_fmaf(q, t, kC * (1.0f / 720.0f));
+    q = __builtin_fmaf(q, t, kC * (1.0f / 120.0f));
+    q = __builtin_fmaf(q, t, kC * (1.0f / 24.0f));
+    q = __builtin_fmaf(q, t, kC * (1.0f / 6.0f));
+    q = __builtin_fmaf(q, t, kC * 0.5f);
+    q = __builtin_fmaf(q, t, 1.0f + kC);
+    const float series = (q * t) * osig;
+    return __builtin_fabsf(t) < 0.25f ? series : direct;
+}
+
+// Per-dtype choice. bf16 needs 2 ulp of an 8-bit significand: the bracket
+// 1 + g(1 - sigma) never comes closer to 0 than 0.0028 on the bf16 grid, so
+// the direct sum (absolute error ~1e-7) is far inside that. fp32 needs 1e-5
+// relative everywhere, including next to g0.
+template <typename T, bool WANT_OSIG>
+__device__ __forceinline__ void sigmoid_pair(float g, float& sig, float& osig) {
+    if constexpr (sizeof(T) == 2) sigmoid_fast<WANT_OSIG>(g, sig, osig);
+    else sigmoid_accurate(g, sig, osig);
 }
 
 template <typename T>
-constexpr bool root_series() {
-    return sizeof(T) == 4 || SWIGLU_ROOT_SERIES_BF16;
+__device__ __forceinline__ float h_factor(float g, float osig) {
+    if constexpr (sizeof(T) == 2) return __builtin_fmaf(g, osig, 1.0f);
+    else return h_root_series(g, osig);
 }
 
 // ---------------------------------------------------------------------------
-// Index walk over the flattened (row, vector) space. Slot k of a lane starts
-// at flat index blockIdx.x*kBlock*kUnroll + k*kBlock + threadIdx.x and
-// advances by the grid's span S = dq*nv + dr each iteration; row and column
-// are carried incrementally so the loop needs no division.
+// Launch geometry. WIDE (n/VEC >= kBlock): block (x, y) owns vectors
+// [x*kBlock, (x+1)*kBlock) of row y. Narrow: block y owns rpb whole rows;
+// lane t takes row t / nv, vector t % nv, computed once in fp32 (exact: both
+// operands are below 256 and the quotient is never within 1/512 of an
+// integer).
 // ---------------------------------------------------------------------------
-struct Walk {
-    int64_t rows;
-    uint32_t nv;     // vectors per half row (n / VEC)
-    uint32_t dq;     // S / nv
-    uint32_t dr;     // S % nv
+struct Geom {
+    int64_t rows;     // rows covered by this launch
+    uint32_t nv;      // vectors per half row (n / VEC)
+    uint32_t rpb;     // rows per block (1 when WIDE)
+    float inv_nv;     // 1 / nv (narrow mode)
 };
 
-struct Slot {
-    int64_t row;
-    uint32_t col;
-};
-
-__device__ __forceinline__ void slot_init(Slot& s, uint32_t idx, const Walk& w) {
-    const uint32_t q = idx / w.nv;
-    s.row = q;
-    s.col = idx - q * w.nv;
-}
-
-__device__ __forceinline__ void slot_step(Slot& s, const Walk& w) {
-    s.row += w.dq;
-    s.col += w.dr;
-    if (s.col >= w.nv) {
-        s.col -= w.nv;
-        s.row += 1;
+template <bool WIDE>
+__device__ __forceinline__ bool locate(const Geom& G, int64_t& row, uint32_t& col) {
+    if constexpr (WIDE) {
+        row = blockIdx.y;
+        col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+        return col < G.nv;
+    } else {
+        const uint32_t t = threadIdx.x;
+        const uint32_t q = (uint32_t)(((float)t + 0.5f) * G.inv_nv);
+        col = t - q * G.nv;
+        row = (int64_t)blockIdx.y * G.rpb + q;
+        return q < G.rpb && row < G.rows;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
-template <typename T, int VEC>
-__device__ __forceinline__ void fwd_one(const T* __restrict__ x, int64_t xs, T* __restrict__ y,
-                                        int64_t ys, int64_t n, const Slot& s,
-                                        float (&g)[VEC], float (&u)[VEC]) {
-    (void)x; (void)xs; (void)n;
-    float out[VEC];
+template <typename T, int VEC, bool WIDE>
+__global__ __launch_bounds__(kBlock) void swiglu_fwd_kernel(
+    const T* __restrict__ x, int64_t xs, T* __restrict__ y, int64_t ys, int64_t n, Geom G) {
+    int64_t row;
+    uint32_t col;
+    if (!locate<WIDE>(G, row, col)) return;
+    const int64_t c = (int64_t)col * VEC;
+    const T* xr = x + row * xs + c;
+    float g[VEC], u[VEC], out[VEC];
+    Vec<T, VEC>::load(xr, g);
+    Vec<T, VEC>::load(xr + n, u);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
         float sig, osig;
-        sigmoid_pair(g[i], sig, osig);
+        sigmoid_pair<T, false>(g[i], sig, osig);
         out[i] = (g[i] * sig) * u[i];
     }
-    Vec<T, VEC>::store(y + s.row * ys + (int64_t)s.col * VEC, out);
+    Vec<T, VEC>::store(y + row * ys + c, out);
 }
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(kBlock) void swiglu_fwd_kernel(
-    const T* __restrict__ x, int64_t xs, T* __restrict__ y, int64_t ys, int64_t n, Walk w) {
-    Slot s[kUnroll];
-    const uint32_t base = blockIdx.x * (uint32_t)(kBlock * kUnroll) + threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) slot_init(s[k], base + k * kBlock, w);
-
-    // Full iterations: the last slot has the largest flat index, so if it is
-    // in range all are.
-    while (s[kUnroll - 1].row < w.rows) {
-        float g[kUnroll][VEC], u[kUnroll][VEC];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const T* xr = x + s[k].row * xs + (int64_t)s[k].col * VEC;
-            Vec<T, VEC>::load(xr, g[k]);
-            Vec<T, VEC>::load(xr + n, u[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            fwd_one<T, VEC>(x, xs, y, ys, n, s[k], g[k], u[k]);
-            slot_step(s[k], w);
-        }
-    }
-    // Last, partial iteration.
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-        if (s[k].row < w.rows) {
-            float g[VEC], u[VEC];
-            const T* xr = x + s[k].row * xs + (int64_t)s[k].col * VEC;
-            Vec<T, VEC>::load(xr, g);
-            Vec<T, VEC>::load(xr + n, u);
-            fwd_one<T, VEC>(x, xs, y, ys, n, s[k], g, u);
-        }
-    }
-}
-
-// One vector of the backward. Reads g, u, dy; writes dgate at dxr and dup at
-// dxr + n. In place, dxr is the same address the gate was read from; every
-// element is read and written by this one lane only, reads first.
-template <typename T, int VEC>
-__device__ __forceinline__ void bwd_one(T* dxr, int64_t n, const float (&g)[VEC],
-                                        const float (&u)[VEC], const float (&dy)[VEC]) {
-    float dg[VEC], du[VEC];
+// IN_PLACE: dx == x (no restrict: the same addresses are read, then written
+// by the same lane; no other lane touches them).
+template <typename T, int VEC, bool WIDE, bool IN_PLACE>
+__global__ __launch_bounds__(kBlock) void swiglu_bwd_kernel(
+    const T* dy, int64_t dys, T* x, int64_t xs, T* dx, int64_t dxs, int64_t n, Geom G) {
+    if constexpr (IN_PLACE) { dx = x; dxs = xs; }
+    int64_t row;
+    uint32_t col;
+    if (!locate<WIDE>(G, row, col)) return;
+    const int64_t c = (int64_t)col * VEC;
+    const T* xr = x + row * xs + c;
+    float g[VEC], u[VEC], d[VEC], dg[VEC], du[VEC];
+    Vec<T, VEC>::load(xr, g);
+    Vec<T, VEC>::load(xr + n, u);
+    Vec<T, VEC>::load(dy + row * dys + c, d);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
         float sig, osig;
-        sigmoid_pair(g[i], sig, osig);
-        const float h = h_factor<root_series<T>()>(g[i], osig);
-        du[i] = dy[i] * (g[i] * sig);
-        dg[i] = ((dy[i] * u[i]) * sig) * h;
+        sigmoid_pair<T, true>(g[i], sig, osig);
+        const float h = h_factor<T>(g[i], osig);
+        du[i] = d[i] * (g[i] * sig);
+        dg[i] = ((d[i] * u[i]) * sig) * h;
     }
+    T* dxr = dx + row * dxs + c;
     Vec<T, VEC>::store(dxr, dg);
     Vec<T, VEC>::store(dxr + n, du);
-}
-
-// IN_PLACE: dx == x (no restrict: the same addresses are read then written).
-template <typename T, int VEC, bool IN_PLACE>
-__global__ __launch_bounds__(kBlock) void swiglu_bwd_kernel(
-    const T* dy, int64_t dys, T* x, int64_t xs, T* dx, int64_t dxs, int64_t n, Walk w) {
-    if constexpr (IN_PLACE) { dx = x; dxs = xs; }
-    Slot s[kUnroll];
-    const uint32_t base = blockIdx.x * (uint32_t)(kBlock * kUnroll) + threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) slot_init(s[k], base + k * kBlock, w);
-
-    while (s[kUnroll - 1].row < w.rows) {
-        float g[kUnroll][VEC], u[kUnroll][VEC], d[kUnroll][VEC];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t c = (int64_t)s[k].col * VEC;
-            const T* xr = x + s[k].row * xs + c;
-            Vec<T, VEC>::load(xr, g[k]);
-            Vec<T, VEC>::load(xr + n, u[k]);
-            Vec<T, VEC>::load(dy + s[k].row * dys + c, d[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t c = (int64_t)s[k].col * VEC;
-            bwd_one<T, VEC>(dx + s[k].row * dxs + c, n, g[k], u[k], d[k]);
-            slot_step(s[k], w);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-        if (s[k].row < w.rows) {
-            float g[VEC], u[VEC], d[VEC];
-            const int64_t c = (int64_t)s[k].col * VEC;
-            const T* xr = x + s[k].row * xs + c;
-            Vec<T, VEC>::load(xr, g);
-            Vec<T, VEC>::load(xr + n, u);
-            Vec<T, VEC>::load(dy + s[k].row * dys + c, d);
-            bwd_one<T, VEC>(dx + s[k].row * dxs + c, n, g, u, d);
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];   // 0 = not yet queried; racing writers store the same value
-
-hipError_t cu_count(int* out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices && g_cu_count[dev] > 0) {
-        *out = g_cu_count[dev];
-        return hipSuccess;
-    }
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (cus <= 0) cus = 1;
-    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev] = cus;
-    *out = cus;
-    return hipSuccess;
-}
-
 struct Span {
     uintptr_t lo, hi;   // [lo, hi) in bytes
 };
@@ -393,8 +333,6 @@ int vec_bytes(int esz, int64_t n, const uintptr_t* ptrs, int nptr, const int64_t
     return b;
 }
 
-// Checks shared by both directions. n is the half width; each (ptr, stride,
-// width) triple describes one [rows, width] operand.
 swiglu_status check_shape(int64_t rows, int64_t n, swiglu_dtype dtype) {
     if (dtype != SWIGLU_DTYPE_F32 && dtype != SWIGLU_DTYPE_BF16) return SWIGLU_ERR_BAD_DTYPE;
     if (rows < 0 || n < 0) return SWIGLU_ERR_BAD_SHAPE;
@@ -402,6 +340,7 @@ swiglu_status check_shape(int64_t rows, int64_t n, swiglu_dtype dtype) {
     return SWIGLU_OK;
 }
 
+// One [rows, width] operand with the given row stride (elements).
 swiglu_status check_operand(int64_t rows, int64_t stride, int64_t width, int64_t esz) {
     if (stride < width) return SWIGLU_ERR_BAD_STRIDE;
     // ((rows - 1) * stride + width) * esz must fit in int64.
@@ -411,59 +350,86 @@ swiglu_status check_operand(int64_t rows, int64_t stride, int64_t width, int64_t
     return SWIGLU_OK;
 }
 
-struct Launch {
-    uint32_t blocks;
-    Walk walk;
+// The rows of one problem are covered by launches of at most kMaxGridY row
+// groups each; launch k starts at row k * kMaxGridY * rpb.
+struct Plan {
+    bool wide;
+    uint32_t nv, rpb, tiles;     // tiles: column tiles per row (WIDE) or 1
+    int64_t rows_per_launch;
 };
 
-hipError_t plan(int64_t rows, int64_t n, int vec, Launch* L) {
-    int cus = 0;
-    hipError_t e = cu_count(&cus);
-    if (e != hipSuccess) return e;
-    const uint64_t nv = (uint64_t)(n / vec);
-    const uint64_t total = (uint64_t)rows * nv;
-    const uint64_t per_block = (uint64_t)kBlock * kUnroll;
-    uint64_t blocks = (total + per_block - 1) / per_block;
-    const uint64_t cap = (uint64_t)cus * SWIGLU_BLOCKS_PER_CU;
-    if (blocks > cap) blocks = cap;
-    if (blocks < 1) blocks = 1;
-    const uint64_t S = blocks * per_block;
-    L->blocks = (uint32_t)blocks;
-    L->walk.rows = rows;
-    L->walk.nv = (uint32_t)nv;
-    L->walk.dq = (uint32_t)(S / nv);
-    L->walk.dr = (uint32_t)(S % nv);
-    return hipSuccess;
+Plan make_plan(int64_t n, int vec) {
+    Plan P;
+    P.nv = (uint32_t)(n / vec);
+    P.wide = P.nv >= (uint32_t)kBlock;
+    P.rpb = P.wide ? 1u : (uint32_t)kBlock / P.nv;
+    P.tiles = P.wide ? (P.nv + kBlock - 1) / kBlock : 1u;
+    P.rows_per_launch = (int64_t)kMaxGridY * P.rpb;
+    return P;
 }
 
-swiglu_status launch(const void* kernel, const Launch& L, void** args, hipStream_t stream) {
-    hipError_t e = hipLaunchKernel(kernel, dim3(L.blocks), dim3(kBlock), args, 0, stream);
-    return e == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP;
+// Launch kernel over rows [0, rows) in chunks; args_for(r0, rcount, G) fills
+// the argument array for the chunk starting at row r0.
+template <typename F>
+swiglu_status launch_chunks(const void* kernel, const Plan& P, int64_t rows, hipStream_t stream,
+                            F&& args_for) {
+    for (int64_t r0 = 0; r0 < rows; r0 += P.rows_per_launch) {
+        const int64_t rc = rows - r0 < P.rows_per_launch ? rows - r0 : P.rows_per_launch;
+        Geom G;
+        G.rows = rc;
+        G.nv = P.nv;
+        G.rpb = P.rpb;
+        G.inv_nv = 1.0f / (float)P.nv;
+        const uint32_t groups = (uint32_t)((rc + P.rpb - 1) / P.rpb);
+        void** args = args_for(r0, G);
+        const hipError_t e =
+            hipLaunchKernel(kernel, dim3(P.tiles, groups), dim3(kBlock), args, 0, stream);
+        if (e != hipSuccess) return SWIGLU_ERR_HIP;
+    }
+    return SWIGLU_OK;
 }
 
 template <typename T, int VEC>
 swiglu_status fwd_launch(const void* x, int64_t xs, void* y, int64_t ys, int64_t rows, int64_t n,
                          hipStream_t stream) {
-    Launch L;
-    if (plan(rows, n, VEC, &L) != hipSuccess) return SWIGLU_ERR_HIP;
-    const T* xp = static_cast<const T*>(x);
-    T* yp = static_cast<T*>(y);
-    void* args[] = {&xp, &xs, &yp, &ys, &n, &L.walk};
-    return launch(reinterpret_cast<const void*>(&swiglu_fwd_kernel<T, VEC>), L, args, stream);
+    const Plan P = make_plan(n, VEC);
+    const void* k = P.wide ? reinterpret_cast<const void*>(&swiglu_fwd_kernel<T, VEC, true>)
+                           : reinterpret_cast<const void*>(&swiglu_fwd_kernel<T, VEC, false>);
+    const T* xp;
+    T* yp;
+    Geom Gc;
+    void* args[] = {&xp, &xs, &yp, &ys, &n, &Gc};
+    return launch_chunks(k, P, rows, stream, [&](int64_t r0, const Geom& G) {
+        xp = static_cast<const T*>(x) + r0 * xs;
+        yp = static_cast<T*>(y) + r0 * ys;
+        Gc = G;
+        return args;
+    });
 }
 
 template <typename T, int VEC>
 swiglu_status bwd_launch(const void* dy, int64_t dys, void* x, int64_t xs, void* dx, int64_t dxs,
                          int64_t rows, int64_t n, bool in_place, hipStream_t stream) {
-    Launch L;
-    if (plan(rows, n, VEC, &L) != hipSuccess) return SWIGLU_ERR_HIP;
-    const T* dyp = static_cast<const T*>(dy);
-    T* xp = static_cast<T*>(x);
-    T* dxp = static_cast<T*>(dx);
-    void* args[] = {&dyp, &dys, &xp, &xs, &dxp, &dxs, &n, &L.walk};
-    const void* k = in_place ? reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, true>)
-                             : reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, false>);
-    return launch(k, L, args, stream);
+    const Plan P = make_plan(n, VEC);
+    const void* k;
+    if (P.wide)
+        k = in_place ? reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, true, true>)
+                     : reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, true, false>);
+    else
+        k = in_place ? reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, false, true>)
+                     : reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, false, false>);
+    const T* dyp;
+    T* xp;
+    T* dxp;
+    Geom Gc;
+    void* args[] = {&dyp, &dys, &xp, &xs, &dxp, &dxs, &n, &Gc};
+    return launch_chunks(k, P, rows, stream, [&](int64_t r0, const Geom& G) {
+        dyp = static_cast<const T*>(dy) + r0 * dys;
+        xp = static_cast<T*>(x) + r0 * xs;
+        dxp = static_cast<T*>(dx) + r0 * dxs;
+        Gc = G;
+        return args;
+    });
 }
 
 }  // namespace
@@ -499,19 +465,21 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_fwd(
     const uintptr_t ptrs[] = {(uintptr_t)x, (uintptr_t)y};
     const int64_t strides[] = {x_row_stride, y_row_stride};
     const int vb = vec_bytes((int)esz, n, ptrs, 2, strides, 2);
+#define SWIGLU_FWD(T, V) fwd_launch<T, V>(x, x_row_stride, y, y_row_stride, rows, n, stream)
     if (dtype == SWIGLU_DTYPE_BF16) {
         switch (vb) {
-            case 16: return fwd_launch<uint16_t, 8>(x, x_row_stride, y, y_row_stride, rows, n, stream);
-            case 8: return fwd_launch<uint16_t, 4>(x, x_row_stride, y, y_row_stride, rows, n, stream);
-            case 4: return fwd_launch<uint16_t, 2>(x, x_row_stride, y, y_row_stride, rows, n, stream);
-            default: return fwd_launch<uint16_t, 1>(x, x_row_stride, y, y_row_stride, rows, n, stream);
+            case 16: return SWIGLU_FWD(uint16_t, 8);
+            case 8: return SWIGLU_FWD(uint16_t, 4);
+            case 4: return SWIGLU_FWD(uint16_t, 2);
+            default: return SWIGLU_FWD(uint16_t, 1);
         }
     }
     switch (vb) {
-        case 16: return fwd_launch<float, 4>(x, x_row_stride, y, y_row_stride, rows, n, stream);
-        case 8: return fwd_launch<float, 2>(x, x_row_stride, y, y_row_stride, rows, n, stream);
-        default: return fwd_launch<float, 1>(x, x_row_stride, y, y_row_stride, rows, n, stream);
+        case 16: return SWIGLU_FWD(float, 4);
+        case 8: return SWIGLU_FWD(float, 2);
+        default: return SWIGLU_FWD(float, 1);
     }
+#undef SWIGLU_FWD
 }
 
 __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bwd(
