@@ -217,6 +217,71 @@ def main():
                                      "bytes": 2 * nbytes, "kind": "torch copy_ (context)"}
         del src, dst
         log(f"[bench] bwd in_place {ip_avg:.4f} ms; copy {cavg:.4f} ms")
+        # The same step through the autograd module (forward + loss-side
+        # backward), and the two-tensor entry points on views of x.
+        from swiglu_activation_amd.autograd import MegatronSwiGLU
+        m = MegatronSwiGLU()
+        xa = x.detach().requires_grad_(True)
+
+        def ag_step():
+            xa.grad = None
+            m(xa).backward(dy)
+
+        for _ in range(3):
+            ag_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            ag_step()
+        torch.cuda.synchronize()
+        ag_ms = (time.perf_counter() - t0) * 1e3 / K
+        passes["autograd_step"] = {"ms": round(ag_ms, 5), "GBps": round(step_bytes / ag_ms / 1e6, 1),
+                                   "what": "MegatronSwiGLU forward + backward via autograd"}
+        del xa
+        gate, upv = x.reshape(w.rows, 2 * w.n)[:, :w.n], x.reshape(w.rows, 2 * w.n)[:, w.n:]
+        dy2 = dy.reshape(w.rows, w.n)
+        y2 = y.reshape(w.rows, w.n)
+        dg2, du2 = dx.reshape(w.rows, 2 * w.n)[:, :w.n], dx.reshape(w.rows, 2 * w.n)[:, w.n:]
+        tt = []
+        for k in range(12):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            sw.swiglu_silu_mul_fwd(gate, upv, y2)
+            b.record(stream)
+            sw.swiglu_silu_mul_bwd(dy2, gate, upv, dg2, du2)
+            c.record(stream)
+            c.synchronize()
+            if k >= 2:
+                tt.append((a.elapsed_time(b), b.elapsed_time(c)))
+        tf, tb = float(np.mean([t[0] for t in tt])), float(np.mean([t[1] for t in tt]))
+        passes["two_tensor_views"] = {"fwd_ms": round(tf, 5), "bwd_ms": round(tb, 5),
+                                      "fwd_GBps": round(fwd_bytes / tf / 1e6, 1),
+                                      "bwd_GBps": round(bwd_bytes / tb / 1e6, 1)}
+        log(f"[bench] autograd step {ag_ms:.4f} ms; two-tensor fwd {tf:.4f} ms bwd {tb:.4f} ms")
+        if (w.n * e) % 16 == 0 and w.rows <= 65535:
+            # The same access patterns with no arithmetic: the best this memory
+            # system streams for each mix, on the same buffers and grid.
+            import ceiling
+            nv16 = w.n * e // 16
+
+            def ceil_ms(pattern, out):
+                ts = []
+                for k in range(22):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    ceiling.launch(pattern, x, dy, out, w.rows, nv16, stream)
+                    b.record(stream)
+                    b.synchronize()
+                    if k >= 2:
+                        ts.append(a.elapsed_time(b))
+                return float(np.mean(ts))
+
+            c0, c1 = ceil_ms(0, y), ceil_ms(1, dx)
+            passes["ceiling_fwd_mix"] = {"ms_avg": round(c0, 5), "GBps": round(fwd_bytes / c0 / 1e6, 1),
+                                         "fwd_frac_of_ceiling": round(c0 / fwd_avg, 4)}
+            passes["ceiling_bwd_mix"] = {"ms_avg": round(c1, 5), "GBps": round(bwd_bytes / c1 / 1e6, 1),
+                                         "bwd_frac_of_ceiling": round(c1 / bwd_avg, 4)}
+            log(f"[bench] ceiling: fwd mix {c0:.4f} ms, bwd mix {c1:.4f} ms")
 
     if args.calib:
         # Known-size plain copies: each reads and writes exactly CALIB_BYTES.

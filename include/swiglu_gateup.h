@@ -29,7 +29,9 @@
  *    asynchronously; a return of SWIGLU_OK means "validated and launched".
  *  - Every argument check happens on the host before anything is launched. On
  *    an error nothing is written and no HIP call is made.
- *  - rows == 0 or n == 0 is a valid empty problem: SWIGLU_OK, no launch.
+ *  - rows == 0 or n == 0 is a valid empty problem: SWIGLU_OK, no launch (the
+ *    dtype, shape and stride checks still apply).
+ *  - n must be below 2^31 (SWIGLU_ERR_BAD_SHAPE otherwise).
  *  - Pointer alignment is never an error: 16-byte vector loads and stores are
  *    used when the base pointers, n and the row strides allow them, narrower
  *    accesses otherwise.
@@ -114,6 +116,53 @@ swiglu_status swiglu_gateup_bwd(const void* dy, int64_t dy_row_stride,
                                 void* dx, int64_t dx_row_stride,
                                 int64_t rows, int64_t n,
                                 swiglu_dtype dtype, int in_place, hipStream_t stream);
+
+/*
+ * Two-tensor forward (Liger-Kernel Megatron SwiGLU page, §Background: Liger's
+ * existing SiLU-times-up op takes gate and up as two separate tensors, the
+ * layout of models whose gate and up projections are separate GEMMs).
+ * Same arithmetic as swiglu_gateup_fwd, on two [rows, n] inputs.
+ *
+ *   gate, up      [rows, n] inputs, read only; each has its own row stride
+ *                 (>= n). They may overlap each other.
+ *   y             [rows, n] output, row stride >= n; must not overlap gate or up.
+ *   rows, n, dtype, stream: as for swiglu_gateup_fwd.
+ *
+ * Errors: SWIGLU_ERR_NULL_POINTER, SWIGLU_ERR_BAD_SHAPE, SWIGLU_ERR_BAD_STRIDE,
+ * SWIGLU_ERR_BAD_DTYPE, SWIGLU_ERR_ALIASING (y overlaps gate or up),
+ * SWIGLU_ERR_HIP.
+ */
+swiglu_status swiglu_silu_mul_fwd(const void* gate, int64_t gate_row_stride,
+                                  const void* up, int64_t up_row_stride,
+                                  void* y, int64_t y_row_stride,
+                                  int64_t rows, int64_t n,
+                                  swiglu_dtype dtype, hipStream_t stream);
+
+/*
+ * Two-tensor backward: dgate = dy * up * sigma(gate) * (1 + gate (1 - sigma(gate))),
+ * dup = dy * silu(gate), each [rows, n].
+ *
+ *   dy            [rows, n], read only, row stride >= n.
+ *   gate, up      [rows, n] saved forward inputs, row strides >= n. Read only
+ *                 when in_place == 0; when in_place != 0 dgate overwrites gate
+ *                 and dup overwrites up.
+ *   dgate, dup    out of place: [rows, n] outputs with their own row strides;
+ *                 they must not overlap each other, dy, gate or up. In place:
+ *                 each must be NULL or equal to gate / up respectively (their
+ *                 strides are then ignored).
+ *   in_place      0 = write dgate, dup; nonzero = overwrite gate and up (which
+ *                 must then not overlap each other or dy).
+ *
+ * Errors: SWIGLU_ERR_NULL_POINTER, SWIGLU_ERR_BAD_SHAPE, SWIGLU_ERR_BAD_STRIDE,
+ * SWIGLU_ERR_BAD_DTYPE, SWIGLU_ERR_ALIASING, SWIGLU_ERR_HIP.
+ */
+swiglu_status swiglu_silu_mul_bwd(const void* dy, int64_t dy_row_stride,
+                                  void* gate, int64_t gate_row_stride,
+                                  void* up, int64_t up_row_stride,
+                                  void* dgate, int64_t dgate_row_stride,
+                                  void* dup, int64_t dup_row_stride,
+                                  int64_t rows, int64_t n,
+                                  swiglu_dtype dtype, int in_place, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* swiglu_status_string(swiglu_status status);

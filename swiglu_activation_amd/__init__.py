@@ -16,7 +16,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_status_string",
+__all__ = ["swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
+           "swiglu_status_string",
            "SwiGLUError", "library_path", "load_library", "EXPORTS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,8 @@ SWIGLU_DTYPE_F32 = 0
 SWIGLU_DTYPE_BF16 = 1
 _BAD_DTYPE_CODE = -1    # passed for any other torch dtype; the library rejects it
 
-EXPORTS = ("swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_status_string")
+EXPORTS = ("swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
+           "swiglu_status_string")
 
 _lib = None
 
@@ -70,6 +72,11 @@ def load_library():
     lib.swiglu_gateup_fwd.restype = cint
     lib.swiglu_gateup_bwd.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, cint, cint, vp]
     lib.swiglu_gateup_bwd.restype = cint
+    lib.swiglu_silu_mul_fwd.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, cint, vp]
+    lib.swiglu_silu_mul_fwd.restype = cint
+    lib.swiglu_silu_mul_bwd.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64,
+                                        cint, cint, vp]
+    lib.swiglu_silu_mul_bwd.restype = cint
     lib.swiglu_status_string.argtypes = [cint]
     lib.swiglu_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -210,3 +217,73 @@ def swiglu_gateup_bwd(dy, x, dx=None, *, in_place: bool = False, stream=None):
                                    _stream_handle(x.device, stream))
     _check(st, "swiglu_gateup_bwd")
     return out
+
+
+def _same_rows(t, rows, n, name):
+    r, s = _rows_and_stride(t, name)
+    if r != rows or t.shape[-1] != n:
+        raise ValueError(f"{name} must hold {rows} rows of {n} elements")
+    return s
+
+
+def swiglu_silu_mul_fwd(gate, up, y=None, *, stream=None):
+    """y = silu(gate) * up for two tensors of the same shape [..., n]."""
+    import torch
+    lib = load_library()
+    _require_device(gate, up, y)
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    if gate.dtype != up.dtype:
+        raise ValueError("gate and up must have the same dtype")
+    n = gate.shape[-1] if gate.dim() else 1
+    rows, gs = _rows_and_stride(gate, "gate")
+    us = _same_rows(up, rows, n, "up")
+    if y is None:
+        y = torch.empty(tuple(gate.shape), dtype=gate.dtype, device=gate.device)
+    if y.dtype != gate.dtype:
+        raise ValueError("y must have the dtype of gate")
+    ys = _same_rows(y, rows, n, "y")
+    with torch.cuda.device(gate.device):
+        st = lib.swiglu_silu_mul_fwd(gate.data_ptr(), gs, up.data_ptr(), us, y.data_ptr(), ys,
+                                     rows, n, _dtype_code(gate), _stream_handle(gate.device, stream))
+    _check(st, "swiglu_silu_mul_fwd")
+    return y
+
+
+def swiglu_silu_mul_bwd(dy, gate, up, dgate=None, dup=None, *, in_place: bool = False, stream=None):
+    """(dgate, dup) for y = silu(gate) * up. With in_place=True they overwrite
+    gate and up, which are returned."""
+    import torch
+    lib = load_library()
+    _require_device(dy, gate, up, dgate, dup)
+    if gate.shape != up.shape or dy.shape != gate.shape:
+        raise ValueError("dy, gate and up must have the same shape")
+    if not (dy.dtype == gate.dtype == up.dtype):
+        raise ValueError("dy, gate and up must have the same dtype")
+    n = gate.shape[-1] if gate.dim() else 1
+    rows, gs = _rows_and_stride(gate, "gate")
+    us = _same_rows(up, rows, n, "up")
+    dys = _same_rows(dy, rows, n, "dy")
+    if in_place:
+        for t, src, name in ((dgate, gate, "dgate"), (dup, up, "dup")):
+            if t is not None and t.data_ptr() != src.data_ptr():
+                raise ValueError(f"in_place backward writes into the inputs; pass {name}=None")
+        dgate, dup = gate, up
+        dg_ptr = du_ptr = None
+        dgs = dus = 0
+    else:
+        if dgate is None:
+            dgate = torch.empty(tuple(gate.shape), dtype=gate.dtype, device=gate.device)
+        if dup is None:
+            dup = torch.empty(tuple(gate.shape), dtype=gate.dtype, device=gate.device)
+        if dgate.dtype != gate.dtype or dup.dtype != gate.dtype:
+            raise ValueError("dgate and dup must have the dtype of gate")
+        dgs = _same_rows(dgate, rows, n, "dgate")
+        dus = _same_rows(dup, rows, n, "dup")
+        dg_ptr, du_ptr = dgate.data_ptr(), dup.data_ptr()
+    with torch.cuda.device(gate.device):
+        st = lib.swiglu_silu_mul_bwd(dy.data_ptr(), dys, gate.data_ptr(), gs, up.data_ptr(), us,
+                                     dg_ptr, dgs, du_ptr, dus, rows, n, _dtype_code(gate),
+                                     1 if in_place else 0, _stream_handle(gate.device, stream))
+    _check(st, "swiglu_silu_mul_bwd")
+    return dgate, dup

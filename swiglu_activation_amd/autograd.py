@@ -1,0 +1,139 @@
+"""Autograd ops and a Megatron-style module over the HIP kernels.
+
+Behaviour follows the Liger-Kernel Megatron SwiGLU page:
+* §Background / §What's added: a differentiable op on the packed fc1 output
+  [..., 2n] (gate first, up second) whose backward recomputes silu from the
+  saved input; only that input is saved.
+* §How to use: the module is called with the positional arguments of
+  Megatron's bias_swiglu_impl -- (intermediate, bias, fp8_input_store,
+  cpu_offload_input) -- so it can stand in for it.
+* §Optional in_place: with in_place=True the backward writes [dgate | dup]
+  over the saved fc1 output instead of a new buffer (opt-in, off by default).
+* §Known issues: writes through a raw pointer do not bump torch's version
+  counter, so a second backward through the same graph (retain_graph=True)
+  would read gradients as if they were activations; the op remembers that
+  its in-place backward ran and raises on a second one.
+* §Scope: bias, FP8 input retention and CPU offload are served by Megatron's
+  own path. There is no Megatron here, so they are errors (the behaviour the
+  page gives for fallback_impl=None).
+* §Background: the two-tensor op for models whose gate and up projections
+  are separate tensors.
+
+Every computation runs in libswiglu_gateup.so; this module only wires it
+into autograd.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import (swiglu_gateup_bwd, swiglu_gateup_fwd, swiglu_silu_mul_bwd,
+               swiglu_silu_mul_fwd, _rows_and_stride)
+
+__all__ = ["FusedGateUpSiLUMul", "SiLUMul", "MegatronSwiGLU", "fused_gate_up_swiglu", "silu_mul"]
+
+
+def _as_row_view(t: torch.Tensor) -> torch.Tensor:
+    """t itself if the kernels can address it as [rows, width] with a single
+    row stride, else a contiguous copy (autograd may hand in expanded or
+    transposed gradients)."""
+    try:
+        _rows_and_stride(t, "t")
+        return t
+    except ValueError:
+        return t.contiguous()
+
+
+class FusedGateUpSiLUMul(torch.autograd.Function):
+    """y = silu(x[..., :n]) * x[..., n:]; dx = [dgate | dup]."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, in_place: bool = False):
+        x = _as_row_view(x)
+        y = swiglu_gateup_fwd(x)
+        ctx.save_for_backward(x)
+        ctx.in_place = bool(in_place)
+        ctx.already_backward = False
+        return y
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        (x,) = ctx.saved_tensors
+        dy = _as_row_view(dy)
+        if ctx.in_place:
+            if ctx.already_backward:
+                raise RuntimeError(
+                    "FusedGateUpSiLUMul: backward called a second time with in_place=True; the "
+                    "first backward overwrote the saved fc1 output with its gradient. Use "
+                    "in_place=False to backpropagate through this graph more than once.")
+            ctx.already_backward = True
+            dx = swiglu_gateup_bwd(dy, x, in_place=True)
+        else:
+            dx = swiglu_gateup_bwd(dy, x)
+        return dx, None
+
+
+class SiLUMul(torch.autograd.Function):
+    """y = silu(gate) * up on two tensors; returns (dgate, dup) in backward."""
+
+    @staticmethod
+    def forward(ctx, gate: torch.Tensor, up: torch.Tensor, in_place: bool = False):
+        gate, up = _as_row_view(gate), _as_row_view(up)
+        y = swiglu_silu_mul_fwd(gate, up)
+        ctx.save_for_backward(gate, up)
+        ctx.in_place = bool(in_place)
+        ctx.already_backward = False
+        return y
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        gate, up = ctx.saved_tensors
+        dy = _as_row_view(dy)
+        if ctx.in_place:
+            if ctx.already_backward:
+                raise RuntimeError(
+                    "SiLUMul: backward called a second time with in_place=True; the first "
+                    "backward overwrote the saved gate and up with their gradients.")
+            ctx.already_backward = True
+        dgate, dup = swiglu_silu_mul_bwd(dy, gate, up, in_place=ctx.in_place)
+        return dgate, dup, None
+
+
+def fused_gate_up_swiglu(x: torch.Tensor, in_place: bool = False) -> torch.Tensor:
+    return FusedGateUpSiLUMul.apply(x, in_place)
+
+
+def silu_mul(gate: torch.Tensor, up: torch.Tensor, in_place: bool = False) -> torch.Tensor:
+    return SiLUMul.apply(gate, up, in_place)
+
+
+class MegatronSwiGLU(torch.nn.Module):
+    """Drop-in for Megatron's bias_swiglu_impl on the packed [s, b, 2n] or
+    [tokens, 2n] fc1 output.
+
+    Called as module(intermediate, bias, fp8_input_store, cpu_offload_input)
+    with the same positional order. Only bias=None, fp8_input_store=False and
+    cpu_offload_input=False are served; anything else raises
+    NotImplementedError.
+    """
+
+    def __init__(self, in_place: bool = False):
+        super().__init__()
+        self.in_place = bool(in_place)
+
+    def extra_repr(self) -> str:
+        return f"in_place={self.in_place}"
+
+    def forward(self, intermediate: torch.Tensor, bias=None, fp8_input_store: bool = False,
+                cpu_offload_input: bool = False) -> torch.Tensor:
+        if bias is not None:
+            raise NotImplementedError("MegatronSwiGLU: a bias on the fc1 output is not supported")
+        if fp8_input_store:
+            raise NotImplementedError("MegatronSwiGLU: fp8_input_store=True is not supported")
+        if cpu_offload_input:
+            raise NotImplementedError("MegatronSwiGLU: cpu_offload_input=True is not supported")
+        if intermediate.dim() not in (2, 3):
+            raise ValueError(f"MegatronSwiGLU: expected a 2D or 3D input, got {intermediate.dim()}D")
+        if intermediate.shape[-1] % 2:
+            raise ValueError("MegatronSwiGLU: the last dimension must be 2 * ffn_hidden (even)")
+        return FusedGateUpSiLUMul.apply(intermediate, self.in_place)

@@ -1,0 +1,91 @@
+// Host-side argument logic of the SwiGLU library: operand views, overlap
+// tests, access-width choice and launch planning. Plain C++ (no HIP), so it
+// is also compiled on its own by the CPU tests.
+#ifndef SWIGLU_HOST_LOGIC_H
+#define SWIGLU_HOST_LOGIC_H
+
+#include <stdint.h>
+
+namespace swiglu_host {
+
+// One [rows, width] operand: base pointer and row stride, both in elements.
+struct Operand {
+    const void* p;
+    int64_t stride;
+};
+
+struct Span {
+    uintptr_t lo, hi;   // [lo, hi) in bytes
+};
+
+inline Span span_of(Operand o, int64_t rows, int64_t width, int64_t esz) {
+    const uintptr_t lo = (uintptr_t)o.p;
+    return {lo, lo + (uintptr_t)(((rows - 1) * o.stride + width) * esz)};
+}
+
+inline bool spans_overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+inline __int128 floor_div(__int128 a, __int128 b) {   // b > 0
+    __int128 q = a / b;
+    if ((a % b != 0) && (a < 0)) q -= 1;
+    return q;
+}
+
+// Do two [rows, wa] and [rows, wb] views share at least one byte?
+// Exact when both have the same row stride (the case of views into one
+// buffer, such as the two halves of a packed [rows, 2n] tensor): row i of A
+// and row j of B intersect iff -WB < d + (j - i) s < WA, with d the byte
+// offset of B from A, s the byte stride and WA, WB the byte widths, so the
+// views overlap iff an integer k = j - i in [-(rows-1), rows-1] satisfies it.
+// With different strides the answer is conservative (any overlap of the
+// spans counts).
+inline bool views_overlap(Operand a, int64_t wa, Operand b, int64_t wb, int64_t rows,
+                          int64_t esz) {
+    if (rows <= 0 || wa <= 0 || wb <= 0) return false;
+    if (!spans_overlap(span_of(a, rows, wa, esz), span_of(b, rows, wb, esz))) return false;
+    if (rows == 1 || a.stride != b.stride) return true;
+    const __int128 s = (__int128)a.stride * esz;
+    const __int128 d = (__int128)(uintptr_t)b.p - (__int128)(uintptr_t)a.p;
+    const __int128 WA = (__int128)wa * esz, WB = (__int128)wb * esz;
+    __int128 klo = floor_div(-WB - d, s) + 1;          // smallest k with d + k s > -WB
+    __int128 khi = -floor_div(-(WA - d), s) - 1;       // largest k with d + k s < WA
+    if (klo < -(__int128)(rows - 1)) klo = -(__int128)(rows - 1);
+    if (khi > (__int128)(rows - 1)) khi = (__int128)(rows - 1);
+    return klo <= khi;
+}
+
+// Largest per-lane access (16, 8, 4 or 2 bytes; at least one element) that
+// every operand's base pointer and row stride are aligned to.
+inline int vec_bytes(int esz, const Operand* ops, int nops) {
+    int b = 16;
+    for (; b > esz; b >>= 1) {
+        bool ok = true;
+        for (int i = 0; i < nops; ++i)
+            ok = ok && ((uintptr_t)ops[i].p % (uintptr_t)b) == 0 && ((ops[i].stride * esz) % b) == 0;
+        if (ok) break;
+    }
+    return b;
+}
+
+// Launch plan. WIDE (n/VEC >= block): block (x, y) owns vectors
+// [x*block, (x+1)*block) of row y. Narrow: block y owns rpb = block / nv
+// whole rows. Rows are covered by launches of at most max_grid_y row groups.
+struct Plan {
+    bool wide;
+    uint32_t nv, rpb, tiles;     // tiles: column tiles per row (WIDE) or 1
+    int64_t rows_per_launch;
+};
+
+inline Plan make_plan(int64_t n, int vec, uint32_t block, uint32_t max_grid_y) {
+    Plan P;
+    P.nv = (uint32_t)(n / vec);
+    P.wide = P.nv >= block;
+    P.rpb = P.wide ? 1u : block / P.nv;
+    P.tiles = P.wide ? (P.nv + block - 1) / block : 1u;
+    P.rows_per_launch = (int64_t)max_grid_y * P.rpb;
+    return P;
+}
+
+}  // namespace swiglu_host
+
+#endif  // SWIGLU_HOST_LOGIC_H

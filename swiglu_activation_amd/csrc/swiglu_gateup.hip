@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include "swiglu_gateup.h"
+#include "host_logic.h"
 
 #ifndef SWIGLU_NT_LOAD
 #define SWIGLU_NT_LOAD 1        // nontemporal hint on loads
@@ -255,19 +256,23 @@ __device__ __forceinline__ bool locate(const Geom& G, int64_t& row, uint32_t& co
 }
 
 // ---------------------------------------------------------------------------
-// Kernels
+// Kernels. The gate and up operands are two [rows, n] views with their own
+// base pointers and row strides: the packed layout is the case up = x + n
+// with both strides equal to x's, and the two-tensor layout passes two
+// tensors. Row offsets are uniform per block, so the extra base costs no
+// lane arithmetic.
 // ---------------------------------------------------------------------------
 template <typename T, int VEC, bool WIDE>
 __global__ __launch_bounds__(kBlock) void swiglu_fwd_kernel(
-    const T* __restrict__ x, int64_t xs, T* __restrict__ y, int64_t ys, int64_t n, Geom G) {
+    const T* __restrict__ gp, int64_t gs, const T* __restrict__ up, int64_t us,
+    T* __restrict__ y, int64_t ys, Geom G) {
     int64_t row;
     uint32_t col;
     if (!locate<WIDE>(G, row, col)) return;
     const int64_t c = (int64_t)col * VEC;
-    const T* xr = x + row * xs + c;
     float g[VEC], u[VEC], out[VEC];
-    Vec<T, VEC>::load(xr, g);
-    Vec<T, VEC>::load(xr + n, u);
+    Vec<T, VEC>::load(gp + row * gs + c, g);
+    Vec<T, VEC>::load(up + row * us + c, u);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
         float sig, osig;
@@ -277,21 +282,26 @@ __global__ __launch_bounds__(kBlock) void swiglu_fwd_kernel(
     Vec<T, VEC>::store(y + row * ys + c, out);
 }
 
-// IN_PLACE: dx == x (no restrict: the same addresses are read, then written
-// by the same lane; no other lane touches them).
+// IN_PLACE: dgate over gate and dup over up (no restrict: the same addresses
+// are read, then written by the same lane; no other lane touches them).
 template <typename T, int VEC, bool WIDE, bool IN_PLACE>
 __global__ __launch_bounds__(kBlock) void swiglu_bwd_kernel(
-    const T* dy, int64_t dys, T* x, int64_t xs, T* dx, int64_t dxs, int64_t n, Geom G) {
-    if constexpr (IN_PLACE) { dx = x; dxs = xs; }
+    const T* dyp, int64_t dys, T* gp, int64_t gs, T* up, int64_t us,
+    T* dgp, int64_t dgs, T* dup, int64_t dus, Geom G) {
+    if constexpr (IN_PLACE) {
+        dgp = gp;
+        dgs = gs;
+        dup = up;
+        dus = us;
+    }
     int64_t row;
     uint32_t col;
     if (!locate<WIDE>(G, row, col)) return;
     const int64_t c = (int64_t)col * VEC;
-    const T* xr = x + row * xs + c;
     float g[VEC], u[VEC], d[VEC], dg[VEC], du[VEC];
-    Vec<T, VEC>::load(xr, g);
-    Vec<T, VEC>::load(xr + n, u);
-    Vec<T, VEC>::load(dy + row * dys + c, d);
+    Vec<T, VEC>::load(gp + row * gs + c, g);
+    Vec<T, VEC>::load(up + row * us + c, u);
+    Vec<T, VEC>::load(dyp + row * dys + c, d);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
         float sig, osig;
@@ -300,38 +310,17 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_kernel(
         du[i] = d[i] * (g[i] * sig);
         dg[i] = ((d[i] * u[i]) * sig) * h;
     }
-    T* dxr = dx + row * dxs + c;
-    Vec<T, VEC>::store(dxr, dg);
-    Vec<T, VEC>::store(dxr + n, du);
+    Vec<T, VEC>::store(dgp + row * dgs + c, dg);
+    Vec<T, VEC>::store(dup + row * dus + c, du);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-struct Span {
-    uintptr_t lo, hi;   // [lo, hi) in bytes
-};
-
-Span span_of(const void* p, int64_t rows, int64_t stride, int64_t width, int64_t esz) {
-    const uintptr_t lo = (uintptr_t)p;
-    return {lo, lo + (uintptr_t)(((rows - 1) * stride + width) * esz)};
-}
-
-bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
-
-// Largest per-lane access (16, 8, 4 or 2 bytes; at least one element) that
-// every base pointer, the up-half offset and every row stride are aligned to.
-int vec_bytes(int esz, int64_t n, const uintptr_t* ptrs, int nptr, const int64_t* strides,
-              int nstr) {
-    int b = 16;
-    for (; b > esz; b >>= 1) {
-        bool ok = ((n * esz) % b) == 0;
-        for (int i = 0; i < nptr; ++i) ok = ok && (ptrs[i] % (uintptr_t)b) == 0;
-        for (int i = 0; i < nstr; ++i) ok = ok && ((strides[i] * esz) % b) == 0;
-        if (ok) break;
-    }
-    return b;
-}
+using swiglu_host::Operand;
+using swiglu_host::Plan;
+using swiglu_host::vec_bytes;
+using swiglu_host::views_overlap;
 
 swiglu_status check_shape(int64_t rows, int64_t n, swiglu_dtype dtype) {
     if (dtype != SWIGLU_DTYPE_F32 && dtype != SWIGLU_DTYPE_BF16) return SWIGLU_ERR_BAD_DTYPE;
@@ -350,38 +339,35 @@ swiglu_status check_operand(int64_t rows, int64_t stride, int64_t width, int64_t
     return SWIGLU_OK;
 }
 
-// The rows of one problem are covered by launches of at most kMaxGridY row
-// groups each; launch k starts at row k * kMaxGridY * rpb.
-struct Plan {
-    bool wide;
-    uint32_t nv, rpb, tiles;     // tiles: column tiles per row (WIDE) or 1
-    int64_t rows_per_launch;
-};
-
 Plan make_plan(int64_t n, int vec) {
-    Plan P;
-    P.nv = (uint32_t)(n / vec);
-    P.wide = P.nv >= (uint32_t)kBlock;
-    P.rpb = P.wide ? 1u : (uint32_t)kBlock / P.nv;
-    P.tiles = P.wide ? (P.nv + kBlock - 1) / kBlock : 1u;
-    P.rows_per_launch = (int64_t)kMaxGridY * P.rpb;
-    return P;
+    return swiglu_host::make_plan(n, vec, (uint32_t)kBlock, kMaxGridY);
 }
 
-// Launch kernel over rows [0, rows) in chunks; args_for(r0, rcount, G) fills
-// the argument array for the chunk starting at row r0.
-template <typename F>
-swiglu_status launch_chunks(const void* kernel, const Plan& P, int64_t rows, hipStream_t stream,
-                            F&& args_for) {
+// Launch `kernel` over rows [0, rows) in chunks. The argument array holds, in
+// order, (pointer, stride) pairs for each operand followed by the Geom; each
+// chunk advances every pointer by r0 rows.
+template <typename T, int NOPS>
+swiglu_status launch_chunks(const void* kernel, const Plan& P, int64_t rows, const Operand* ops,
+                            hipStream_t stream) {
+    T* ptr[NOPS];
+    int64_t stride[NOPS];
+    Geom G;
+    void* args[2 * NOPS + 1];
+    for (int i = 0; i < NOPS; ++i) {
+        stride[i] = ops[i].stride;
+        args[2 * i] = &ptr[i];
+        args[2 * i + 1] = &stride[i];
+    }
+    args[2 * NOPS] = &G;
+    G.nv = P.nv;
+    G.rpb = P.rpb;
+    G.inv_nv = 1.0f / (float)P.nv;
     for (int64_t r0 = 0; r0 < rows; r0 += P.rows_per_launch) {
         const int64_t rc = rows - r0 < P.rows_per_launch ? rows - r0 : P.rows_per_launch;
-        Geom G;
+        for (int i = 0; i < NOPS; ++i)
+            ptr[i] = const_cast<T*>(static_cast<const T*>(ops[i].p)) + r0 * ops[i].stride;
         G.rows = rc;
-        G.nv = P.nv;
-        G.rpb = P.rpb;
-        G.inv_nv = 1.0f / (float)P.nv;
         const uint32_t groups = (uint32_t)((rc + P.rpb - 1) / P.rpb);
-        void** args = args_for(r0, G);
         const hipError_t e =
             hipLaunchKernel(kernel, dim3(P.tiles, groups), dim3(kBlock), args, 0, stream);
         if (e != hipSuccess) return SWIGLU_ERR_HIP;
@@ -389,27 +375,19 @@ swiglu_status launch_chunks(const void* kernel, const Plan& P, int64_t rows, hip
     return SWIGLU_OK;
 }
 
+// ops: gate, up, y.
 template <typename T, int VEC>
-swiglu_status fwd_launch(const void* x, int64_t xs, void* y, int64_t ys, int64_t rows, int64_t n,
-                         hipStream_t stream) {
+swiglu_status fwd_launch(const Operand* ops, int64_t rows, int64_t n, hipStream_t stream) {
     const Plan P = make_plan(n, VEC);
     const void* k = P.wide ? reinterpret_cast<const void*>(&swiglu_fwd_kernel<T, VEC, true>)
                            : reinterpret_cast<const void*>(&swiglu_fwd_kernel<T, VEC, false>);
-    const T* xp;
-    T* yp;
-    Geom Gc;
-    void* args[] = {&xp, &xs, &yp, &ys, &n, &Gc};
-    return launch_chunks(k, P, rows, stream, [&](int64_t r0, const Geom& G) {
-        xp = static_cast<const T*>(x) + r0 * xs;
-        yp = static_cast<T*>(y) + r0 * ys;
-        Gc = G;
-        return args;
-    });
+    return launch_chunks<T, 3>(k, P, rows, ops, stream);
 }
 
+// ops: dy, gate, up, dgate, dup.
 template <typename T, int VEC>
-swiglu_status bwd_launch(const void* dy, int64_t dys, void* x, int64_t xs, void* dx, int64_t dxs,
-                         int64_t rows, int64_t n, bool in_place, hipStream_t stream) {
+swiglu_status bwd_launch(const Operand* ops, int64_t rows, int64_t n, bool in_place,
+                         hipStream_t stream) {
     const Plan P = make_plan(n, VEC);
     const void* k;
     if (P.wide)
@@ -418,18 +396,54 @@ swiglu_status bwd_launch(const void* dy, int64_t dys, void* x, int64_t xs, void*
     else
         k = in_place ? reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, false, true>)
                      : reinterpret_cast<const void*>(&swiglu_bwd_kernel<T, VEC, false, false>);
-    const T* dyp;
-    T* xp;
-    T* dxp;
-    Geom Gc;
-    void* args[] = {&dyp, &dys, &xp, &xs, &dxp, &dxs, &n, &Gc};
-    return launch_chunks(k, P, rows, stream, [&](int64_t r0, const Geom& G) {
-        dyp = static_cast<const T*>(dy) + r0 * dys;
-        xp = static_cast<T*>(x) + r0 * xs;
-        dxp = static_cast<T*>(dx) + r0 * dxs;
-        Gc = G;
-        return args;
-    });
+    return launch_chunks<T, 5>(k, P, rows, ops, stream);
+}
+
+// Validated forward on [rows, n] views: gate, up -> y.
+swiglu_status run_fwd(Operand gate, Operand up, Operand y, int64_t rows, int64_t n,
+                      swiglu_dtype dtype, hipStream_t stream) {
+    const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
+    const Operand ops[3] = {gate, up, y};
+    const int vb = vec_bytes((int)esz, ops, 3);
+    if (dtype == SWIGLU_DTYPE_BF16) {
+        switch (vb) {
+            case 16: return fwd_launch<uint16_t, 8>(ops, rows, n, stream);
+            case 8: return fwd_launch<uint16_t, 4>(ops, rows, n, stream);
+            case 4: return fwd_launch<uint16_t, 2>(ops, rows, n, stream);
+            default: return fwd_launch<uint16_t, 1>(ops, rows, n, stream);
+        }
+    }
+    switch (vb) {
+        case 16: return fwd_launch<float, 4>(ops, rows, n, stream);
+        case 8: return fwd_launch<float, 2>(ops, rows, n, stream);
+        default: return fwd_launch<float, 1>(ops, rows, n, stream);
+    }
+}
+
+// Validated backward on [rows, n] views: dy, gate, up -> dgate, dup.
+swiglu_status run_bwd(Operand dy, Operand gate, Operand up, Operand dgate, Operand dup,
+                      int64_t rows, int64_t n, swiglu_dtype dtype, bool in_place,
+                      hipStream_t stream) {
+    const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
+    const Operand ops[5] = {dy, gate, up, dgate, dup};
+    const int vb = vec_bytes((int)esz, ops, 5);
+    if (dtype == SWIGLU_DTYPE_BF16) {
+        switch (vb) {
+            case 16: return bwd_launch<uint16_t, 8>(ops, rows, n, in_place, stream);
+            case 8: return bwd_launch<uint16_t, 4>(ops, rows, n, in_place, stream);
+            case 4: return bwd_launch<uint16_t, 2>(ops, rows, n, in_place, stream);
+            default: return bwd_launch<uint16_t, 1>(ops, rows, n, in_place, stream);
+        }
+    }
+    switch (vb) {
+        case 16: return bwd_launch<float, 4>(ops, rows, n, in_place, stream);
+        case 8: return bwd_launch<float, 2>(ops, rows, n, in_place, stream);
+        default: return bwd_launch<float, 1>(ops, rows, n, in_place, stream);
+    }
+}
+
+const void* offset(const void* p, int64_t elems, int64_t esz) {
+    return p ? static_cast<const char*>(p) + elems * esz : nullptr;
 }
 
 }  // namespace
@@ -459,27 +473,9 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_fwd(
     if ((st = check_operand(rows, y_row_stride, n, esz)) != SWIGLU_OK) return st;
     if (rows == 0 || n == 0) return SWIGLU_OK;
     if (!x || !y) return SWIGLU_ERR_NULL_POINTER;
-    if (overlaps(span_of(x, rows, x_row_stride, 2 * n, esz), span_of(y, rows, y_row_stride, n, esz)))
-        return SWIGLU_ERR_ALIASING;
-
-    const uintptr_t ptrs[] = {(uintptr_t)x, (uintptr_t)y};
-    const int64_t strides[] = {x_row_stride, y_row_stride};
-    const int vb = vec_bytes((int)esz, n, ptrs, 2, strides, 2);
-#define SWIGLU_FWD(T, V) fwd_launch<T, V>(x, x_row_stride, y, y_row_stride, rows, n, stream)
-    if (dtype == SWIGLU_DTYPE_BF16) {
-        switch (vb) {
-            case 16: return SWIGLU_FWD(uint16_t, 8);
-            case 8: return SWIGLU_FWD(uint16_t, 4);
-            case 4: return SWIGLU_FWD(uint16_t, 2);
-            default: return SWIGLU_FWD(uint16_t, 1);
-        }
-    }
-    switch (vb) {
-        case 16: return SWIGLU_FWD(float, 4);
-        case 8: return SWIGLU_FWD(float, 2);
-        default: return SWIGLU_FWD(float, 1);
-    }
-#undef SWIGLU_FWD
+    const Operand ox{x, x_row_stride}, oy{y, y_row_stride};
+    if (views_overlap(ox, 2 * n, oy, n, rows, esz)) return SWIGLU_ERR_ALIASING;
+    return run_fwd(ox, Operand{offset(x, n, esz), x_row_stride}, oy, rows, n, dtype, stream);
 }
 
 __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bwd(
@@ -500,34 +496,71 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bwd(
     if ((st = check_operand(rows, dx_row_stride, 2 * n, esz)) != SWIGLU_OK) return st;
     if (rows == 0 || n == 0) return SWIGLU_OK;
     if (!dy || !x || !dx) return SWIGLU_ERR_NULL_POINTER;
-    const Span sdy = span_of(dy, rows, dy_row_stride, n, esz);
-    const Span sx = span_of(x, rows, x_row_stride, 2 * n, esz);
-    if (ip) {
-        if (overlaps(sdy, sx)) return SWIGLU_ERR_ALIASING;
-    } else {
-        const Span sdx = span_of(dx, rows, dx_row_stride, 2 * n, esz);
-        if (overlaps(sdx, sx) || overlaps(sdx, sdy)) return SWIGLU_ERR_ALIASING;
-    }
+    const Operand ody{dy, dy_row_stride}, ox{x, x_row_stride}, odx{dx, dx_row_stride};
+    if (views_overlap(ody, n, ox, 2 * n, rows, esz)) return SWIGLU_ERR_ALIASING;
+    if (!ip && (views_overlap(odx, 2 * n, ox, 2 * n, rows, esz) ||
+                views_overlap(odx, 2 * n, ody, n, rows, esz)))
+        return SWIGLU_ERR_ALIASING;
+    return run_bwd(ody, ox, Operand{offset(x, n, esz), x_row_stride}, odx,
+                   Operand{offset(dx, n, esz), dx_row_stride}, rows, n, dtype, ip, stream);
+}
 
-    const uintptr_t ptrs[] = {(uintptr_t)dy, (uintptr_t)x, (uintptr_t)dx};
-    const int64_t strides[] = {dy_row_stride, x_row_stride, dx_row_stride};
-    const int vb = vec_bytes((int)esz, n, ptrs, 3, strides, 3);
-#define SWIGLU_BWD(T, V) \
-    bwd_launch<T, V>(dy, dy_row_stride, x, x_row_stride, dx, dx_row_stride, rows, n, ip, stream)
-    if (dtype == SWIGLU_DTYPE_BF16) {
-        switch (vb) {
-            case 16: return SWIGLU_BWD(uint16_t, 8);
-            case 8: return SWIGLU_BWD(uint16_t, 4);
-            case 4: return SWIGLU_BWD(uint16_t, 2);
-            default: return SWIGLU_BWD(uint16_t, 1);
-        }
+__attribute__((visibility("default"))) swiglu_status swiglu_silu_mul_fwd(
+    const void* gate, int64_t gate_row_stride, const void* up, int64_t up_row_stride, void* y,
+    int64_t y_row_stride, int64_t rows, int64_t n, swiglu_dtype dtype, hipStream_t stream) {
+    swiglu_status st = check_shape(rows, n, dtype);
+    if (st != SWIGLU_OK) return st;
+    const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
+    if ((st = check_operand(rows, gate_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, up_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, y_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if (rows == 0 || n == 0) return SWIGLU_OK;
+    if (!gate || !up || !y) return SWIGLU_ERR_NULL_POINTER;
+    const Operand og{gate, gate_row_stride}, ou{up, up_row_stride}, oy{y, y_row_stride};
+    if (views_overlap(oy, n, og, n, rows, esz) || views_overlap(oy, n, ou, n, rows, esz))
+        return SWIGLU_ERR_ALIASING;
+    return run_fwd(og, ou, oy, rows, n, dtype, stream);
+}
+
+__attribute__((visibility("default"))) swiglu_status swiglu_silu_mul_bwd(
+    const void* dy, int64_t dy_row_stride, void* gate, int64_t gate_row_stride, void* up,
+    int64_t up_row_stride, void* dgate, int64_t dgate_row_stride, void* dup,
+    int64_t dup_row_stride, int64_t rows, int64_t n, swiglu_dtype dtype, int in_place,
+    hipStream_t stream) {
+    swiglu_status st = check_shape(rows, n, dtype);
+    if (st != SWIGLU_OK) return st;
+    const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
+    const bool ip = in_place != 0;
+    if (ip) {
+        if ((dgate != nullptr && dgate != gate) || (dup != nullptr && dup != up))
+            return SWIGLU_ERR_ALIASING;
+        dgate = gate;
+        dgate_row_stride = gate_row_stride;
+        dup = up;
+        dup_row_stride = up_row_stride;
     }
-    switch (vb) {
-        case 16: return SWIGLU_BWD(float, 4);
-        case 8: return SWIGLU_BWD(float, 2);
-        default: return SWIGLU_BWD(float, 1);
+    if ((st = check_operand(rows, dy_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, gate_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, up_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, dgate_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, dup_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if (rows == 0 || n == 0) return SWIGLU_OK;
+    if (!dy || !gate || !up || !dgate || !dup) return SWIGLU_ERR_NULL_POINTER;
+    const Operand ody{dy, dy_row_stride}, og{gate, gate_row_stride}, ou{up, up_row_stride},
+        odg{dgate, dgate_row_stride}, odu{dup, dup_row_stride};
+    if (ip) {
+        // both inputs are written: they must not overlap each other or dy
+        if (views_overlap(og, n, ou, n, rows, esz) || views_overlap(ody, n, og, n, rows, esz) ||
+            views_overlap(ody, n, ou, n, rows, esz))
+            return SWIGLU_ERR_ALIASING;
+    } else {
+        if (views_overlap(odg, n, odu, n, rows, esz)) return SWIGLU_ERR_ALIASING;
+        for (const Operand& o : {odg, odu})
+            if (views_overlap(o, n, ody, n, rows, esz) || views_overlap(o, n, og, n, rows, esz) ||
+                views_overlap(o, n, ou, n, rows, esz))
+                return SWIGLU_ERR_ALIASING;
     }
-#undef SWIGLU_BWD
+    return run_bwd(ody, og, ou, odg, odu, rows, n, dtype, ip, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,30 @@
+"""Argument handling of the module wrapper that needs no GPU."""
+
+import pytest
+import torch
+
+from swiglu_activation_amd.autograd import MegatronSwiGLU
+
+
+def test_unsupported_options_raise():
+    m = MegatronSwiGLU()
+    x = torch.zeros(4, 8)
+    with pytest.raises(NotImplementedError):
+        m(x, torch.zeros(8))
+    with pytest.raises(NotImplementedError):
+        m(x, None, True)
+    with pytest.raises(NotImplementedError):
+        m(x, None, False, True)
+
+
+def test_shape_validation():
+    m = MegatronSwiGLU(in_place=True)
+    assert "in_place=True" in repr(m)
+    with pytest.raises(ValueError):
+        m(torch.zeros(8))              # 1D
+    with pytest.raises(ValueError):
+        m(torch.zeros(2, 2, 2, 8))     # 4D
+    with pytest.raises(ValueError):
+        m(torch.zeros(4, 7))           # odd last dim
+    with pytest.raises(ValueError):
+        m(torch.zeros(4, 8))           # host tensor: device pointers only

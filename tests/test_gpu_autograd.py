@@ -1,0 +1,172 @@
+"""Autograd ops, the module wrapper and the two-tensor layout (needs an MI355X)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swiglu_activation_amd as sw
+from swiglu_activation_amd.autograd import MegatronSwiGLU, fused_gate_up_swiglu, silu_mul
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(rows, n, dtype, seed):
+    rng = np.random.default_rng(seed)
+    g, u, d = rng.standard_normal((3, rows, n))
+    g *= 3
+    if dtype == "fp32":
+        return np.concatenate([g, u], 1).astype(np.float32), d.astype(np.float32)
+    return (oracle.round_f64_to_bf16_bits(np.concatenate([g, u], 1)),
+            oracle.round_f64_to_bf16_bits(d))
+
+
+def _refs(x_h, dy_h, dtype):
+    xf, dyf = oracle.widen(x_h, dtype), oracle.widen(dy_h, dtype)
+    return oracle.oracle_fwd(xf), oracle.oracle_bwd(xf, dyf)
+
+
+def _check(got, ref, dtype, what):
+    st = gu.compare(gu.from_dev(got).reshape(ref.shape), ref, dtype, what)
+    print("   ", st, flush=True)
+    assert st.ok(), str(st)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_module_forward_backward_parity(dtype, in_place):
+    print(f"[autograd] {dtype} in_place={in_place}", flush=True)
+    x_h, dy_h = _case(3 * 40, 384, dtype, seed=11)
+    yref, dref = _refs(x_h, dy_h, dtype)
+    x = gu.to_dev(x_h, dtype).reshape(3, 40, 768).requires_grad_(True)
+    dy = gu.to_dev(dy_h, dtype).reshape(3, 40, 384)
+    m = MegatronSwiGLU(in_place=in_place)
+    y = m(x, None, False, False)
+    assert y.shape == (3, 40, 384)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    _check(y.detach(), yref, dtype, "fwd")
+    _check(x.grad, dref, dtype, "bwd")
+    if in_place:
+        # the backward wrote [dgate | dup] over the saved fc1 output itself
+        assert gu.bits_equal(x.detach(), x.grad)
+
+
+def test_in_place_second_backward_raises():
+    x_h, dy_h = _case(16, 256, "bf16", seed=12)
+    x = gu.to_dev(x_h, "bf16").requires_grad_(True)
+    dy = gu.to_dev(dy_h, "bf16")
+    y = fused_gate_up_swiglu(x, True)
+    y.backward(dy, retain_graph=True)
+    with pytest.raises(RuntimeError, match="second time"):
+        y.backward(dy)
+    torch.cuda.synchronize()
+
+
+def test_out_of_place_backward_repeats():
+    x_h, dy_h = _case(16, 256, "bf16", seed=13)
+    x = gu.to_dev(x_h, "bf16").requires_grad_(True)
+    dy = gu.to_dev(dy_h, "bf16")
+    y = fused_gate_up_swiglu(x)
+    y.backward(dy, retain_graph=True)
+    g1 = x.grad.clone()
+    x.grad = None
+    y.backward(dy)
+    torch.cuda.synchronize()
+    assert gu.bits_equal(g1, x.grad)
+
+
+def test_expanded_upstream_gradient():
+    """y.sum() hands the backward an expanded (stride 0) gradient."""
+    x_h, _ = _case(8, 256, "fp32", seed=14)
+    x = gu.to_dev(x_h, "fp32").requires_grad_(True)
+    fused_gate_up_swiglu(x).sum().backward()
+    torch.cuda.synchronize()
+    dref = oracle.oracle_bwd(oracle.widen(x_h, "fp32"), np.ones((8, 256)))
+    _check(x.grad, dref, "fp32", "bwd of sum")
+
+
+def test_mlp_end_to_end_matches_float64_reference():
+    """fc1 -> SwiGLU -> fc2 in fp32 on the GPU against the same MLP in float64
+    on the CPU (torch's own silu there): loss and fc1/fc2 weight gradients."""
+    torch.manual_seed(0)
+    h, f, T = 64, 96, 50
+    fc1 = torch.nn.Linear(h, 2 * f, bias=False)
+    fc2 = torch.nn.Linear(f, h, bias=False)
+    inp = torch.randn(T, h)
+    w1, w2 = fc1.weight.detach().double().requires_grad_(), fc2.weight.detach().double().requires_grad_()
+    z = inp.double() @ w1.t()
+    a = torch.nn.functional.silu(z[:, :f]) * z[:, f:]
+    loss = ((a @ w2.t()) ** 2).mean()
+    loss.backward()
+    ref = (loss.item(), w1.grad, w2.grad)
+    fc1c, fc2c = fc1.cuda(), fc2.cuda()
+    m = MegatronSwiGLU()
+    torch.backends.cuda.matmul.allow_tf32 = False
+    out = fc2c(m(fc1c(inp.cuda())))
+    lg = (out ** 2).mean()
+    lg.backward()
+    torch.cuda.synchronize()
+    # fp32 GEMMs on the GPU accumulate in another order than float64 on the CPU
+    assert abs(lg.item() - ref[0]) <= 1e-4 * abs(ref[0])
+    for got, want in ((fc1c.weight.grad, ref[1]), (fc2c.weight.grad, ref[2])):
+        err = (got.double().cpu() - want).abs().max().item() / want.abs().max().item()
+        assert err < 1e-4, err
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_two_tensor_layout_parity_and_views(dtype):
+    """silu_mul on separate gate/up tensors, on strided views of one packed
+    tensor (no copies), in place and out of place."""
+    print(f"[two-tensor] {dtype}", flush=True)
+    rows, n = 300, 1000
+    x_h, dy_h = _case(rows, n, dtype, seed=15)
+    yref, dref = _refs(x_h, dy_h, dtype)
+    x = gu.to_dev(x_h, dtype)
+    dy = gu.to_dev(dy_h, dtype)
+    gate, up = x[:, :n], x[:, n:]                    # views, row stride 2n
+    y = sw.swiglu_silu_mul_fwd(gate, up)
+    dg, du = sw.swiglu_silu_mul_bwd(dy, gate, up)
+    torch.cuda.synchronize()
+    _check(y, yref, dtype, "fwd")
+    _check(dg, dref[:, :n], dtype, "dgate")
+    _check(du, dref[:, n:], dtype, "dup")
+    # identical bits to the packed entry points
+    assert gu.bits_equal(y, sw.swiglu_gateup_fwd(x))
+    dx = sw.swiglu_gateup_bwd(dy, x)
+    assert gu.bits_equal(dg, dx[:, :n]) and gu.bits_equal(du, dx[:, n:])
+    # outputs as the two interleaved halves of one packed buffer
+    dxb = torch.empty_like(x)
+    sw.swiglu_silu_mul_bwd(dy, gate, up, dxb[:, :n], dxb[:, n:])
+    assert gu.bits_equal(dxb, dx)
+    # in place on the two interleaved halves of one buffer
+    xc = x.clone()
+    sw.swiglu_silu_mul_bwd(dy, xc[:, :n], xc[:, n:], in_place=True)
+    assert gu.bits_equal(xc, dx)
+    # separate contiguous tensors, in place
+    g2, u2 = gate.contiguous(), up.contiguous()
+    dg2, du2 = sw.swiglu_silu_mul_bwd(dy, g2, u2, in_place=True)
+    torch.cuda.synchronize()
+    assert dg2.data_ptr() == g2.data_ptr() and du2.data_ptr() == u2.data_ptr()
+    assert gu.bits_equal(dg2, dg) and gu.bits_equal(du2, du)
+
+
+def test_two_tensor_autograd_and_errors():
+    x_h, dy_h = _case(64, 512, "bf16", seed=16)
+    x = gu.to_dev(x_h, "bf16")
+    gate = x[:, :512].clone().requires_grad_(True)
+    up = x[:, 512:].clone().requires_grad_(True)
+    dy = gu.to_dev(dy_h, "bf16")
+    silu_mul(gate, up).backward(dy)
+    dx = sw.swiglu_gateup_bwd(dy, x)
+    torch.cuda.synchronize()
+    assert gu.bits_equal(gate.grad, dx[:, :512]) and gu.bits_equal(up.grad, dx[:, 512:])
+    with pytest.raises(ValueError):
+        sw.swiglu_silu_mul_fwd(x[:, :512], x[:, 512:], x[:, 256:768])    # y overlaps inputs
+    with pytest.raises(ValueError):
+        sw.swiglu_silu_mul_bwd(dy, x[:, :512], x[:, 256:768], in_place=True)  # written inputs overlap
+    with pytest.raises(ValueError):
+        sw.swiglu_silu_mul_bwd(dy, gate.detach(), up.detach(), dgate=dy)   # dgate overlaps dy
