@@ -16,7 +16,9 @@ from .swiglu import (  # noqa: F401
     bf16_ordinal,
     bf16_ulp_distance,
     oracle_bwd,
+    oracle_bwd_bias_scale,
     oracle_fwd,
+    oracle_fwd_bias_scale,
     round_f64_to_bf16_bits,
     sigmoid,
     silu,

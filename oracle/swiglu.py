@@ -129,6 +129,46 @@ def oracle_bwd(x, dy) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Bias and per-token scale variants
+# --------------------------------------------------------------------------
+# Liger-Kernel Megatron SwiGLU page, §Scope and §Known issues: Megatron's
+# activation takes an optional bias on the fc1 output (bias_swiglu), and MoE
+# routed experts use a per-token-scale-aware version (weighted_bias_swiglu,
+# with per_token_scale). The page names these but gives no formula; the
+# plainest reading, used here, is
+#     z = x + bias          (bias of shape [2n], broadcast over rows)
+#     y[r, c] = s[r] * silu(z[r, c]) * z[r, n + c]
+# with bias = 0 and s = 1 when absent. Its exact gradient is
+#     dz  = the base backward at z with upstream gradient s[r] * dy[r, c]
+#     dx  = dz                      (the bias add is the identity in x)
+#     dbias[k] = sum over r of dz[r, k]
+#     ds[r]    = sum over c of dy[r, c] * silu(z[r, c]) * z[r, n + c]
+
+def oracle_fwd_bias_scale(x, bias=None, scale=None) -> np.ndarray:
+    """y = s * silu(z_gate) * z_up with z = x + bias; float64 [rows, n]."""
+    x = np.asarray(x, dtype=np.float64)
+    x2 = x.reshape(-1, x.shape[-1])
+    z = x2 + (0.0 if bias is None else np.asarray(bias, dtype=np.float64).reshape(1, -1))
+    y = oracle_fwd(z)
+    if scale is not None:
+        y = y * np.asarray(scale, dtype=np.float64).reshape(-1, 1)
+    return y
+
+
+def oracle_bwd_bias_scale(x, dy, bias=None, scale=None):
+    """Returns (dx [rows, 2n], dbias [2n] or None, dscale [rows] or None)."""
+    x = np.asarray(x, dtype=np.float64)
+    x2 = x.reshape(-1, x.shape[-1])
+    z = x2 + (0.0 if bias is None else np.asarray(bias, dtype=np.float64).reshape(1, -1))
+    dy = np.asarray(dy, dtype=np.float64).reshape(z.shape[0], -1)
+    s = None if scale is None else np.asarray(scale, dtype=np.float64).reshape(-1, 1)
+    dx = oracle_bwd(z, dy if s is None else dy * s)
+    dbias = None if bias is None else dx.sum(axis=0)
+    dscale = None if scale is None else (dy * oracle_fwd(z)).sum(axis=1)
+    return dx, dbias, dscale
+
+
+# --------------------------------------------------------------------------
 # Comparison targets
 # --------------------------------------------------------------------------
 

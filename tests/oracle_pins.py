@@ -124,3 +124,53 @@ def pin_layout(impl):
 
 ALL_PINS = [pin_closed_forms, pin_expit, pin_minimiser, pin_symmetry,
             pin_mpmath_derivative, pin_layout]
+
+
+def pin_bias_scale_reduces_to_base(impl):
+    """With bias = 0 and scale = 1 the variants are the base op, and a bias
+    is the same as adding it to x first."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 12)) * 2
+    dy = rng.standard_normal((5, 6))
+    assert np.array_equal(impl.oracle_fwd_bias_scale(x), impl.oracle_fwd(x))
+    dx, db, ds = impl.oracle_bwd_bias_scale(x, dy)
+    assert db is None and ds is None and np.array_equal(dx, impl.oracle_bwd(x, dy))
+    y1 = impl.oracle_fwd_bias_scale(x, np.zeros(12), np.ones(5))
+    assert np.max(np.abs(y1 - impl.oracle_fwd(x))) == 0.0
+    b = rng.standard_normal(12)
+    assert np.array_equal(impl.oracle_fwd_bias_scale(x, b), impl.oracle_fwd(x + b))
+
+
+def pin_bias_scale_finite_differences(impl):
+    """dx, dbias and dscale against central differences of the forward in
+    x, bias and scale (the loss is sum(dy * y))."""
+    rng = np.random.default_rng(32)
+    rows, n = 4, 5
+    x = rng.standard_normal((rows, 2 * n)) * 2
+    b = rng.standard_normal(2 * n)
+    s = rng.uniform(0.2, 2.0, rows)
+    dy = rng.standard_normal((rows, n))
+    dx, db, ds = impl.oracle_bwd_bias_scale(x, dy, b, s)
+
+    def loss(xx, bb, ss):
+        return float(np.sum(dy * impl.oracle_fwd_bias_scale(xx, bb, ss)))
+
+    h = 1e-6
+    for idx in np.ndindex(x.shape):
+        e = np.zeros_like(x)
+        e[idx] = h
+        fd = (loss(x + e, b, s) - loss(x - e, b, s)) / (2 * h)
+        assert abs(fd - dx[idx]) <= 1e-6 * (1 + abs(fd)), ("dx", idx, fd, dx[idx])
+    for k in range(2 * n):
+        e = np.zeros_like(b)
+        e[k] = h
+        fd = (loss(x, b + e, s) - loss(x, b - e, s)) / (2 * h)
+        assert abs(fd - db[k]) <= 1e-6 * (1 + abs(fd)), ("dbias", k, fd, db[k])
+    for r in range(rows):
+        e = np.zeros_like(s)
+        e[r] = h
+        fd = (loss(x, b, s + e) - loss(x, b, s - e)) / (2 * h)
+        assert abs(fd - ds[r]) <= 1e-6 * (1 + abs(fd)), ("dscale", r, fd, ds[r])
+
+
+BIAS_SCALE_PINS = [pin_bias_scale_reduces_to_base, pin_bias_scale_finite_differences]

@@ -21,7 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 def _impl(**over):
     base = dict(sigmoid=oracle.sigmoid, silu=oracle.silu, silu_grad=oracle.silu_grad,
-                oracle_fwd=oracle.oracle_fwd, oracle_bwd=oracle.oracle_bwd)
+                oracle_fwd=oracle.oracle_fwd, oracle_bwd=oracle.oracle_bwd,
+                oracle_fwd_bias_scale=oracle.oracle_fwd_bias_scale,
+                oracle_bwd_bias_scale=oracle.oracle_bwd_bias_scale)
     base.update(over)
     return types.SimpleNamespace(**base)
 
@@ -37,7 +39,7 @@ def _tiny_inputs():
 # The oracle passes every pin
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.BIAS_SCALE_PINS, ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(_impl())
 
@@ -127,6 +129,54 @@ MUTANTS = {
     "grad_is_sigmoid": dict(silu_grad=lambda z: oracle.sigmoid(z)),
     "fwd_missing_up": dict(oracle_fwd=lambda x: oracle.silu(oracle.split_gate_up(x)[0])),
 }
+
+
+def _bs_bwd_mutant(kind):
+    def bwd(x, dy, bias=None, scale=None):
+        dx, db, ds = oracle.oracle_bwd_bias_scale(x, dy, bias, scale)
+        x2 = np.asarray(x, float).reshape(np.asarray(dy).shape[0], -1)
+        z = x2 + (0 if bias is None else np.asarray(bias, float))
+        if kind == "dscale_without_up" and scale is not None:
+            n = z.shape[1] // 2
+            ds = (np.asarray(dy, float) * oracle.silu(z[:, :n])).sum(axis=1)
+        if kind == "dbias_from_unscaled" and bias is not None:
+            db = oracle.oracle_bwd(z, dy).sum(axis=0)
+        if kind == "dx_unscaled":
+            dx = oracle.oracle_bwd(z, dy)
+        return dx, db, ds
+    return bwd
+
+
+def _fwd_scale_inside_silu(x, b=None, s=None):
+    z = np.asarray(x, float) + (0.0 if b is None else np.asarray(b, float))
+    if s is not None:
+        n = z.shape[1] // 2
+        z = z.copy()
+        z[:, :n] *= np.asarray(s, float)[:, None]
+    return oracle.oracle_fwd(z)
+
+
+BS_MUTANTS = {
+    "bias_ignored": dict(oracle_fwd_bias_scale=lambda x, b=None, s=None:
+                         oracle.oracle_fwd_bias_scale(x, None, s)),
+    "scale_inside_silu": dict(oracle_fwd_bias_scale=_fwd_scale_inside_silu),
+    "dscale_without_up": dict(oracle_bwd_bias_scale=_bs_bwd_mutant("dscale_without_up")),
+    "dbias_from_unscaled": dict(oracle_bwd_bias_scale=_bs_bwd_mutant("dbias_from_unscaled")),
+    "dx_unscaled": dict(oracle_bwd_bias_scale=_bs_bwd_mutant("dx_unscaled")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BS_MUTANTS))
+def test_planted_bias_scale_mistake_is_caught(name):
+    impl = _impl(**BS_MUTANTS[name])
+    caught = 0
+    for pin in pins.BIAS_SCALE_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl)
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"mutant {name} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
