@@ -258,6 +258,32 @@ def main():
                                       "fwd_GBps": round(fwd_bytes / tf / 1e6, 1),
                                       "bwd_GBps": round(bwd_bytes / tb / 1e6, 1)}
         log(f"[bench] autograd step {ag_ms:.4f} ms; two-tensor fwd {tf:.4f} ms bwd {tb:.4f} ms")
+        # Bias + per-token scale variants on the same tensors: forward, and
+        # backward with dx, dbias and dscale (the reductions included).
+        gen = torch.Generator(device=dev).manual_seed(w.seed)
+        bias_t = (torch.randn(2 * w.n, device=dev, generator=gen) * 0.5).to(tdt)
+        scale_t = torch.rand(w.shape[:-1], device=dev, generator=gen) * 0.95 + 0.05
+        ws = torch.empty(sw.swiglu_gateup_bias_scale_workspace_size(w.rows, w.n, True, True),
+                         dtype=torch.uint8, device=dev)
+        bt = []
+        for k in range(12):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            sw.swiglu_gateup_bias_scale_fwd(x, bias_t, scale_t, y)
+            b.record(stream)
+            sw.swiglu_gateup_bias_scale_bwd(dy, x, bias_t, scale_t, dx, workspace=ws)
+            c.record(stream)
+            c.synchronize()
+            if k >= 2:
+                bt.append((a.elapsed_time(b), b.elapsed_time(c)))
+        bf, bb = float(np.mean([t[0] for t in bt])), float(np.mean([t[1] for t in bt]))
+        passes["bias_scale"] = {"fwd_ms": round(bf, 5), "bwd_ms": round(bb, 5),
+                                "fwd_GBps": round(fwd_bytes / bf / 1e6, 1),
+                                "bwd_GBps": round(bwd_bytes / bb / 1e6, 1),
+                                "what": "z = x + bias, y = s * silu(z_g) * z_u; bwd writes dx, dbias, "
+                                        "dscale (GB/s on the base op's bytes)"}
+        log(f"[bench] bias+scale fwd {bf:.4f} ms, bwd {bb:.4f} ms")
+        del ws
         if (w.n * e) % 16 == 0 and w.rows <= 65535:
             # The same access patterns with no arithmetic: the best this memory
             # system streams for each mix, on the same buffers and grid.

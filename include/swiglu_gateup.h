@@ -42,6 +42,7 @@
 #ifndef SWIGLU_GATEUP_H
 #define SWIGLU_GATEUP_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -62,7 +63,8 @@ typedef enum {
     SWIGLU_ERR_BAD_STRIDE = 3,    /* a row stride is smaller than its row's width */
     SWIGLU_ERR_BAD_DTYPE = 4,     /* dtype is neither SWIGLU_DTYPE_F32 nor SWIGLU_DTYPE_BF16 */
     SWIGLU_ERR_ALIASING = 5,      /* outputs overlap inputs where that is not allowed */
-    SWIGLU_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed */
+    SWIGLU_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
+    SWIGLU_ERR_WORKSPACE = 7      /* a needed workspace is NULL, too small or not 16-byte aligned */
 } swiglu_status;
 
 /*
@@ -163,6 +165,77 @@ swiglu_status swiglu_silu_mul_bwd(const void* dy, int64_t dy_row_stride,
                                   void* dup, int64_t dup_row_stride,
                                   int64_t rows, int64_t n,
                                   swiglu_dtype dtype, int in_place, hipStream_t stream);
+
+/*
+ * Bias and per-token scale variants (Liger-Kernel Megatron SwiGLU page,
+ * §Scope and §Known issues: Megatron's activation may take a bias on the fc1
+ * output, and MoE routed experts use a version weighted by a per-token
+ * scale; the page names both and prints no formula). With
+ *     z = x + bias                     (bias: [2n], the same for every row)
+ *     y[r, c] = s[r] * silu(z[r, c]) * z[r, n + c]
+ * and bias = 0 / s = 1 when the pointer is NULL, the backward writes
+ *     dx    = dz, the base backward at z with upstream gradient s[r] * dy
+ *     dbias = sum over rows of dx                            ([2n], fp32)
+ *     ds[r] = sum over c of dy[r, c] * silu(z[r, c]) * z[r, n + c]  ([rows], fp32)
+ * The sums are accumulated in fp32 from the fp32 values of dz (before any
+ * rounding to bf16) in a fixed order, so results are bitwise deterministic.
+ *
+ * Forward:
+ *   x, x_row_stride, y, y_row_stride, rows, n, dtype, stream: as in
+ *                 swiglu_gateup_fwd.
+ *   bias          NULL or [2n] elements of dtype (gate part, then up part).
+ *   scale         NULL or fp32 per row: s[r] = scale[r * scale_stride];
+ *                 scale_stride >= 1 when scale is given.
+ * Errors: as swiglu_gateup_fwd; also SWIGLU_ERR_BAD_STRIDE (scale_stride < 1
+ * with a scale) and SWIGLU_ERR_ALIASING (y overlaps bias or scale).
+ */
+swiglu_status swiglu_gateup_bias_scale_fwd(const void* x, int64_t x_row_stride,
+                                           const void* bias, const float* scale,
+                                           int64_t scale_stride,
+                                           void* y, int64_t y_row_stride,
+                                           int64_t rows, int64_t n,
+                                           swiglu_dtype dtype, hipStream_t stream);
+
+/*
+ * Bytes of workspace swiglu_gateup_bias_scale_bwd needs for a problem of
+ * this size when dbias (want_dbias != 0) and/or ds (want_dscale != 0) are
+ * requested; 0 when neither is, and for empty or invalid sizes. The value
+ * does not depend on pointers or dtype.
+ */
+size_t swiglu_gateup_bias_scale_workspace_size(int64_t rows, int64_t n,
+                                               int want_dbias, int want_dscale);
+
+/*
+ * Backward of swiglu_gateup_bias_scale_fwd.
+ *
+ *   dy, x, dx, their strides, rows, n, dtype, in_place, stream: as in
+ *                 swiglu_gateup_bwd (dx receives dz; in place it overwrites x).
+ *   bias, scale, scale_stride: as in the forward.
+ *   dbias         NULL (not wanted) or [2n] fp32 output; needs bias.
+ *   dscale        NULL (not wanted) or fp32 per row, at dscale[r * dscale_stride]
+ *                 (dscale_stride >= 1); needs scale.
+ *   workspace     device memory of at least
+ *                 swiglu_gateup_bias_scale_workspace_size(rows, n, dbias != NULL,
+ *                 dscale != NULL) bytes, 16-byte aligned; may be NULL when that
+ *                 size is 0. Its contents need no initialisation and are
+ *                 scratch afterwards; calls that share a workspace must not run
+ *                 concurrently.
+ * With rows == 0, dbias (if given) is set to zero; with n == 0, ds (if given)
+ * is set to zero; nothing else is launched for empty problems.
+ * Errors: as swiglu_gateup_bwd; also SWIGLU_ERR_NULL_POINTER (dbias without
+ * bias, dscale without scale), SWIGLU_ERR_BAD_STRIDE (scale or dscale stride
+ * < 1), SWIGLU_ERR_WORKSPACE, and SWIGLU_ERR_ALIASING when an output (dx,
+ * dbias, dscale, workspace) overlaps an input or another output.
+ */
+swiglu_status swiglu_gateup_bias_scale_bwd(const void* dy, int64_t dy_row_stride,
+                                           void* x, int64_t x_row_stride,
+                                           const void* bias, const float* scale,
+                                           int64_t scale_stride,
+                                           void* dx, int64_t dx_row_stride,
+                                           float* dbias, float* dscale, int64_t dscale_stride,
+                                           void* workspace, size_t workspace_bytes,
+                                           int64_t rows, int64_t n,
+                                           swiglu_dtype dtype, int in_place, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* swiglu_status_string(swiglu_status status);

@@ -17,7 +17,8 @@ import ctypes
 import os
 
 __all__ = ["swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
-           "swiglu_status_string",
+           "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
+           "swiglu_gateup_bias_scale_workspace_size", "swiglu_status_string",
            "SwiGLUError", "library_path", "load_library", "EXPORTS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -31,12 +32,14 @@ SWIGLU_ERR_BAD_STRIDE = 3
 SWIGLU_ERR_BAD_DTYPE = 4
 SWIGLU_ERR_ALIASING = 5
 SWIGLU_ERR_HIP = 6
+SWIGLU_ERR_WORKSPACE = 7
 SWIGLU_DTYPE_F32 = 0
 SWIGLU_DTYPE_BF16 = 1
 _BAD_DTYPE_CODE = -1    # passed for any other torch dtype; the library rejects it
 
 EXPORTS = ("swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
-           "swiglu_status_string")
+           "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
+           "swiglu_gateup_bias_scale_workspace_size", "swiglu_status_string")
 
 _lib = None
 
@@ -77,6 +80,13 @@ def load_library():
     lib.swiglu_silu_mul_bwd.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64,
                                         cint, cint, vp]
     lib.swiglu_silu_mul_bwd.restype = cint
+    lib.swiglu_gateup_bias_scale_fwd.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, cint, vp]
+    lib.swiglu_gateup_bias_scale_fwd.restype = cint
+    lib.swiglu_gateup_bias_scale_workspace_size.argtypes = [i64, i64, cint, cint]
+    lib.swiglu_gateup_bias_scale_workspace_size.restype = ctypes.c_size_t
+    lib.swiglu_gateup_bias_scale_bwd.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp,
+                                                 i64, vp, ctypes.c_size_t, i64, i64, cint, cint, vp]
+    lib.swiglu_gateup_bias_scale_bwd.restype = cint
     lib.swiglu_status_string.argtypes = [cint]
     lib.swiglu_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -287,3 +297,128 @@ def swiglu_silu_mul_bwd(dy, gate, up, dgate=None, dup=None, *, in_place: bool = 
                                      1 if in_place else 0, _stream_handle(gate.device, stream))
     _check(st, "swiglu_silu_mul_bwd")
     return dgate, dup
+
+
+# ---------------------------------------------------------------------------
+# Bias and per-token scale variants
+# ---------------------------------------------------------------------------
+
+def _bias_arg(bias, x, n):
+    if bias is None:
+        return None
+    _require_device(bias, x)
+    if bias.dim() != 1 or bias.shape[0] != 2 * n or (n and bias.stride(0) != 1):
+        raise ValueError(f"bias must be a contiguous [{2 * n}] tensor")
+    if bias.dtype != x.dtype:
+        raise ValueError("bias must have the dtype of x")
+    return bias.data_ptr()
+
+
+def _per_row_arg(t, x, rows, name):
+    """A per-row fp32 tensor shaped like x's leading dims, optionally with a
+    trailing 1: (pointer, stride)."""
+    import torch
+    if t is None:
+        return None, 1
+    _require_device(t, x)
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    lead = tuple(x.shape[:-1])
+    if tuple(t.shape) == lead:
+        t2 = t.unsqueeze(-1)
+    elif tuple(t.shape) == lead + (1,):
+        t2 = t
+    else:
+        raise ValueError(f"{name} must have shape {lead} or {lead + (1,)}")
+    r, s_ = _rows_and_stride(t2, name)
+    assert r == rows
+    return t.data_ptr(), max(1, s_)
+
+
+def swiglu_gateup_bias_scale_workspace_size(rows: int, n: int, want_dbias: bool,
+                                            want_dscale: bool) -> int:
+    return int(load_library().swiglu_gateup_bias_scale_workspace_size(
+        int(rows), int(n), int(bool(want_dbias)), int(bool(want_dscale))))
+
+
+def swiglu_gateup_bias_scale_fwd(x, bias=None, scale=None, y=None, *, stream=None):
+    """y = scale * silu(z[..., :n]) * z[..., n:] with z = x + bias.
+
+    bias: [2n] of x's dtype or None; scale: float32 per row (shape
+    x.shape[:-1], optionally with a trailing 1) or None."""
+    import torch
+    lib = load_library()
+    _require_device(x, y)
+    if x.dim() < 1 or x.shape[-1] % 2:
+        raise ValueError("last dimension of x must be even (2n)")
+    n = x.shape[-1] // 2
+    rows, xs = _rows_and_stride(x, "x")
+    bp = _bias_arg(bias, x, n)
+    sp, ss = _per_row_arg(scale, x, rows, "scale")
+    if y is None:
+        y = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    if y.dtype != x.dtype:
+        raise ValueError("x and y must have the same dtype")
+    ys = _same_rows(y, rows, n, "y")
+    with torch.cuda.device(x.device):
+        st = lib.swiglu_gateup_bias_scale_fwd(x.data_ptr(), xs, bp, sp, ss, y.data_ptr(), ys, rows,
+                                              n, _dtype_code(x), _stream_handle(x.device, stream))
+    _check(st, "swiglu_gateup_bias_scale_fwd")
+    return y
+
+
+def swiglu_gateup_bias_scale_bwd(dy, x, bias=None, scale=None, dx=None, *, want_dbias=None,
+                                 want_dscale=None, in_place: bool = False, workspace=None,
+                                 stream=None):
+    """Backward of swiglu_gateup_bias_scale_fwd: returns (dx, dbias, dscale).
+
+    dbias ([2n] float32) is computed when want_dbias (default: bias given),
+    dscale (float32, shaped like scale) when want_dscale (default: scale
+    given). workspace: a device tensor of at least
+    swiglu_gateup_bias_scale_workspace_size(...) bytes, allocated if None."""
+    import torch
+    lib = load_library()
+    _require_device(dy, x, dx)
+    if x.dim() < 1 or x.shape[-1] % 2:
+        raise ValueError("last dimension of x must be even (2n)")
+    n = x.shape[-1] // 2
+    if dy.dtype != x.dtype:
+        raise ValueError("dy and x must have the same dtype")
+    rows, xs = _rows_and_stride(x, "x")
+    dys = _same_rows(dy, rows, n, "dy")
+    bp = _bias_arg(bias, x, n)
+    sp, ss = _per_row_arg(scale, x, rows, "scale")
+    want_dbias = bias is not None if want_dbias is None else bool(want_dbias)
+    want_dscale = scale is not None if want_dscale is None else bool(want_dscale)
+    dbias = torch.empty(2 * n, dtype=torch.float32, device=x.device) if want_dbias else None
+    dscale = (torch.empty(tuple(scale.shape), dtype=torch.float32, device=x.device)
+              if want_dscale and scale is not None else None)
+    if want_dscale and scale is None:
+        dscale = torch.empty(tuple(x.shape[:-1]), dtype=torch.float32, device=x.device)
+    dsp, dss = _per_row_arg(dscale, x, rows, "dscale") if dscale is not None else (None, 1)
+    if in_place:
+        if dx is not None and dx.data_ptr() != x.data_ptr():
+            raise ValueError("in_place backward writes into x; pass dx=None or dx=x")
+        dx_ptr, dxs, out = None, 0, x
+    else:
+        if dx is None:
+            dx = torch.empty(tuple(x.shape), dtype=x.dtype, device=x.device)
+        if dx.dtype != x.dtype:
+            raise ValueError("dx and x must have the same dtype")
+        dxs = _same_rows(dx, rows, 2 * n, "dx")
+        dx_ptr, out = dx.data_ptr(), dx
+    need = swiglu_gateup_bias_scale_workspace_size(rows, n, want_dbias, want_dscale)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _require_device(workspace, x)
+        wp, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        wp, wb = None, 0
+    with torch.cuda.device(x.device):
+        st = lib.swiglu_gateup_bias_scale_bwd(
+            dy.data_ptr(), dys, x.data_ptr(), xs, bp, sp, ss, dx_ptr, dxs,
+            dbias.data_ptr() if dbias is not None else None, dsp, dss, wp, wb, rows, n,
+            _dtype_code(x), 1 if in_place else 0, _stream_handle(x.device, stream))
+    _check(st, "swiglu_gateup_bias_scale_bwd")
+    return out, dbias, dscale

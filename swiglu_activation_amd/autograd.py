@@ -13,9 +13,11 @@ Behaviour follows the Liger-Kernel Megatron SwiGLU page:
   counter, so a second backward through the same graph (retain_graph=True)
   would read gradients as if they were activations; the op remembers that
   its in-place backward ran and raises on a second one.
-* §Scope: bias, FP8 input retention and CPU offload are served by Megatron's
-  own path. There is no Megatron here, so they are errors (the behaviour the
-  page gives for fallback_impl=None).
+* §Scope: FP8 input retention and CPU offload are served by Megatron's own
+  path. There is no Megatron here, so they are errors (the behaviour the
+  page gives for fallback_impl=None). A bias on the fc1 output, which the
+  page also leaves to Megatron, is served here by the bias kernels, and so is
+  the per-token-scale (router-weighted) form the page lists as a follow-up.
 * §Background: the two-tensor op for models whose gate and up projections
   are separate tensors.
 
@@ -27,10 +29,11 @@ from __future__ import annotations
 
 import torch
 
-from . import (swiglu_gateup_bwd, swiglu_gateup_fwd, swiglu_silu_mul_bwd,
-               swiglu_silu_mul_fwd, _rows_and_stride)
+from . import (swiglu_gateup_bias_scale_bwd, swiglu_gateup_bias_scale_fwd, swiglu_gateup_bwd,
+               swiglu_gateup_fwd, swiglu_silu_mul_bwd, swiglu_silu_mul_fwd, _rows_and_stride)
 
-__all__ = ["FusedGateUpSiLUMul", "SiLUMul", "MegatronSwiGLU", "fused_gate_up_swiglu", "silu_mul"]
+__all__ = ["FusedGateUpSiLUMul", "FusedGateUpSiLUMulBiasScale", "SiLUMul", "MegatronSwiGLU",
+           "fused_gate_up_swiglu", "silu_mul", "weighted_swiglu"]
 
 
 def _as_row_view(t: torch.Tensor) -> torch.Tensor:
@@ -99,6 +102,45 @@ class SiLUMul(torch.autograd.Function):
         return dgate, dup, None
 
 
+class FusedGateUpSiLUMulBiasScale(torch.autograd.Function):
+    """y = s * silu(z[..., :n]) * z[..., n:] with z = x + bias; bias ([2n])
+    and the per-token scale s (shape x.shape[:-1], or with a trailing 1) are
+    optional. Gradients for x, bias and s."""
+
+    @staticmethod
+    def forward(ctx, x, bias, scale, in_place: bool = False):
+        x = _as_row_view(x)
+        s32 = None
+        if scale is not None:
+            s32 = scale if scale.dtype == torch.float32 else scale.float()
+        y = swiglu_gateup_bias_scale_fwd(x, bias, s32)
+        ctx.save_for_backward(x, bias, s32)
+        ctx.scale_dtype = None if scale is None else scale.dtype
+        ctx.in_place = bool(in_place)
+        ctx.already_backward = False
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, bias, s32 = ctx.saved_tensors
+        dy = _as_row_view(dy)
+        if ctx.in_place:
+            if ctx.already_backward:
+                raise RuntimeError(
+                    "FusedGateUpSiLUMulBiasScale: backward called a second time with "
+                    "in_place=True; the first backward overwrote the saved fc1 output.")
+            ctx.already_backward = True
+        want_db = bias is not None and ctx.needs_input_grad[1]
+        want_ds = s32 is not None and ctx.needs_input_grad[2]
+        dx, dbias, dscale = swiglu_gateup_bias_scale_bwd(
+            dy, x, bias, s32, want_dbias=want_db, want_dscale=want_ds, in_place=ctx.in_place)
+        if dbias is not None:
+            dbias = dbias.to(bias.dtype)
+        if dscale is not None:
+            dscale = dscale.to(ctx.scale_dtype)
+        return dx, dbias, dscale, None
+
+
 def fused_gate_up_swiglu(x: torch.Tensor, in_place: bool = False) -> torch.Tensor:
     return FusedGateUpSiLUMul.apply(x, in_place)
 
@@ -107,14 +149,20 @@ def silu_mul(gate: torch.Tensor, up: torch.Tensor, in_place: bool = False) -> to
     return SiLUMul.apply(gate, up, in_place)
 
 
+def weighted_swiglu(x: torch.Tensor, weights: torch.Tensor, bias=None,
+                    in_place: bool = False) -> torch.Tensor:
+    """Per-token-scaled fused SwiGLU for MoE routed experts:
+    weights * silu(z[..., :n]) * z[..., n:], z = x + bias (bias optional)."""
+    return FusedGateUpSiLUMulBiasScale.apply(x, bias, weights, in_place)
+
+
 class MegatronSwiGLU(torch.nn.Module):
     """Drop-in for Megatron's bias_swiglu_impl on the packed [s, b, 2n] or
     [tokens, 2n] fc1 output.
 
     Called as module(intermediate, bias, fp8_input_store, cpu_offload_input)
-    with the same positional order. Only bias=None, fp8_input_store=False and
-    cpu_offload_input=False are served; anything else raises
-    NotImplementedError.
+    with the same positional order. bias ([2n]) may be None or a tensor;
+    fp8_input_store=True and cpu_offload_input=True raise NotImplementedError.
     """
 
     def __init__(self, in_place: bool = False):
@@ -126,8 +174,6 @@ class MegatronSwiGLU(torch.nn.Module):
 
     def forward(self, intermediate: torch.Tensor, bias=None, fp8_input_store: bool = False,
                 cpu_offload_input: bool = False) -> torch.Tensor:
-        if bias is not None:
-            raise NotImplementedError("MegatronSwiGLU: a bias on the fc1 output is not supported")
         if fp8_input_store:
             raise NotImplementedError("MegatronSwiGLU: fp8_input_store=True is not supported")
         if cpu_offload_input:
@@ -136,4 +182,6 @@ class MegatronSwiGLU(torch.nn.Module):
             raise ValueError(f"MegatronSwiGLU: expected a 2D or 3D input, got {intermediate.dim()}D")
         if intermediate.shape[-1] % 2:
             raise ValueError("MegatronSwiGLU: the last dimension must be 2 * ffn_hidden (even)")
+        if bias is not None:
+            return FusedGateUpSiLUMulBiasScale.apply(intermediate, bias, None, self.in_place)
         return FusedGateUpSiLUMul.apply(intermediate, self.in_place)

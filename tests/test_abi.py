@@ -175,3 +175,54 @@ def test_kernel_constants_match_their_definitions():
         assert (_hex_const(src, "kG0Hi"), _hex_const(src, "kG0Lo")) == split(g0)
         assert _hex_const(src, "kC") == float(np.float32(float(mpmath.exp(g0))))
         assert abs(float(mpmath.exp(g0) + 1 + g0)) < 1e-40
+
+
+def bsf(lib, x, xs, bias, scale, ss, y, ys, rows, n, dt=BF16):
+    return lib.swiglu_gateup_bias_scale_fwd(x, xs, bias, scale, ss, y, ys, rows, n, dt, None)
+
+
+def bsb(lib, dy, dys, x, xs, bias, scale, ss, dx, dxs, db, ds, dss, ws, wsb, rows, n, dt=BF16, ip=0):
+    return lib.swiglu_gateup_bias_scale_bwd(dy, dys, x, xs, bias, scale, ss, dx, dxs, db, ds, dss,
+                                            ws, wsb, rows, n, dt, ip, None)
+
+
+def test_bias_scale_workspace_size(lib):
+    ws = lambda r, n, b, s: lib.swiglu_gateup_bias_scale_workspace_size(r, n, b, s)  # noqa: E731
+    r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert ws(8192, 32768, 0, 0) == 0
+    assert ws(0, 32768, 1, 1) == 0 and ws(8, 0, 1, 1) == 0 and ws(-1, 8, 1, 1) == 0
+    groups = (8192 + 127) // 128
+    assert ws(8192, 32768, 1, 0) == r256(groups * 2 * 32768 * 4)
+    assert ws(8192, 32768, 0, 1) == r256(8192 * 128 * 4)
+    assert ws(8192, 32768, 1, 1) == r256(groups * 2 * 32768 * 4) + r256(8192 * 128 * 4)
+    assert ws(300, 1001, 1, 1) == r256(3 * 2002 * 4) + r256(300 * 4 * 4)
+
+
+@no_gpu_only
+def test_bias_scale_validation(lib):
+    D = 0x2100000   # dbias / dscale / workspace fake addresses far from A, B, C
+    assert bsf(lib, A, 16, B, None, 1, C, 8, 4, 8, dt=9) == sw.SWIGLU_ERR_BAD_DTYPE
+    assert bsf(lib, A, 16, B, C + 4096, 0, C, 8, 4, 8) == sw.SWIGLU_ERR_BAD_STRIDE   # scale stride
+    assert bsf(lib, A, 16, None, None, 1, A + 8, 8, 4, 8) == sw.SWIGLU_ERR_ALIASING   # y over x
+    assert bsf(lib, A, 16, C + 8, None, 1, C, 8, 4, 8) == sw.SWIGLU_ERR_ALIASING     # y over bias
+    # dbias without bias, dscale without scale
+    assert bsb(lib, A, 8, B, 16, None, None, 1, C, 16, D, None, 1, D + 4096, 1 << 20, 4, 8) == \
+        sw.SWIGLU_ERR_NULL_POINTER
+    assert bsb(lib, A, 8, B, 16, None, None, 1, C, 16, None, D, 1, D + 4096, 1 << 20, 4, 8) == \
+        sw.SWIGLU_ERR_NULL_POINTER
+    # workspace missing / too small / misaligned
+    bias = D + (1 << 16)
+    assert bsb(lib, A, 8, B, 16, bias, None, 1, C, 16, D, None, 1, None, 0, 4, 8) == \
+        sw.SWIGLU_ERR_WORKSPACE
+    assert bsb(lib, A, 8, B, 16, bias, None, 1, C, 16, D, None, 1, D + 8192, 16, 4, 8) == \
+        sw.SWIGLU_ERR_WORKSPACE
+    assert bsb(lib, A, 8, B, 16, bias, None, 1, C, 16, D, None, 1, D + 8200, 1 << 20, 4, 8) == \
+        sw.SWIGLU_ERR_WORKSPACE
+    # dbias overlapping the workspace, dx overlapping bias
+    assert bsb(lib, A, 8, B, 16, bias, None, 1, C, 16, D, None, 1, D, 1 << 20, 4, 8) == \
+        sw.SWIGLU_ERR_ALIASING
+    assert bsb(lib, A, 8, B, 16, C + 32, None, 1, C, 16, D, None, 1, D + 8192, 1 << 20, 4, 8) == \
+        sw.SWIGLU_ERR_ALIASING
+    # dscale stride below 1
+    assert bsb(lib, A, 8, B, 16, None, bias, 1, C, 16, None, D, 0, D + 8192, 1 << 20, 4, 8) == \
+        sw.SWIGLU_ERR_BAD_STRIDE

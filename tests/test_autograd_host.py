@@ -10,8 +10,6 @@ def test_unsupported_options_raise():
     m = MegatronSwiGLU()
     x = torch.zeros(4, 8)
     with pytest.raises(NotImplementedError):
-        m(x, torch.zeros(8))
-    with pytest.raises(NotImplementedError):
         m(x, None, True)
     with pytest.raises(NotImplementedError):
         m(x, None, False, True)
