@@ -33,7 +33,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fused SwiGLU fwd+bwd achieved HBM GB/s (and % of peak) at S=2048,B=4,n=32768 bf16"
 PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 CALIB_BYTES = 1 << 30
-KERNEL_SRC = os.path.join(ROOT, "swiglu_activation_amd", "csrc", "swiglu_gateup.hip")
+# Sources of the forward and backward kernels timed here (the traffic record
+# is only used while they are unchanged).
+KERNEL_SRCS = [os.path.join(ROOT, "swiglu_activation_amd", "csrc", f)
+               for f in ("swiglu_gateup.hip", "swiglu_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "swiglu_bwd_wide_bf16_n32768_traffic.txt")
 
 
@@ -42,8 +45,11 @@ def log(*a):
 
 
 def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():

@@ -1,4 +1,4 @@
-"""Compile the HIP library in-tree: csrc/swiglu_gateup.hip -> libswiglu_gateup.so.
+"""Compile the HIP library in-tree: csrc/*.hip -> libswiglu_gateup.so.
 
 gfx950 only. Packed-fp32 instruction selection is switched off for the device
 code (``-packed-fp32-ops``); the host pass prints a harmless warning about the
@@ -14,7 +14,8 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "swiglu_gateup.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", "swiglu_gateup.hip"),
+        os.path.join(PKG_DIR, "csrc", "swiglu_bias_scale.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libswiglu_gateup.so")
 ARCH = "gfx950"
@@ -27,12 +28,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (needs ROCm)")
 
 
-def compile_command(out: str = LIB, src: str = SRC, defines=()) -> list:
+def compile_command(out: str = LIB, srcs=None, defines=()) -> list:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
            "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-I", INCLUDE]
     cmd += [f"-D{d}" for d in defines]
-    cmd += ["-o", out, src]
+    cmd += ["-o", out, *(SRCS if srcs is None else srcs)]
     return cmd
 
 

@@ -1,0 +1,478 @@
+// Bias and per-token-scale variants of the fused gate-up SwiGLU for AMD
+// MI355X (gfx950), with their C ABI (include/swiglu_gateup.h).
+//
+// What is computed (Liger-Kernel Megatron SwiGLU page, §Scope and §Known
+// issues name a bias on the fc1 output and a per-token-scale-aware version
+// for MoE routed experts, without a formula): z = x + bias, y = s * silu(z_g)
+// * z_u; the backward writes dx and the fp32 sums dbias (over rows) and
+// ds (over columns). The elementwise part streams like the base kernels; the
+// sums go through fixed-order partials in a caller-provided workspace, so
+// results are bitwise deterministic.
+#include "swiglu_device.h"
+
+namespace {
+
+using namespace swiglu_impl;
+// ---------------------------------------------------------------------------
+// Bias and per-token scale variants. With z = x + bias (bias: [2n], added to
+// every row) and a per-row scale s (fp32):
+//   forward   y = s * silu(z_gate) * z_up
+//   backward  dz = the base backward at z with upstream gradient s * dy,
+//             dx = dz, dbias = sum over rows of dz, ds = sum over columns of
+//             dy * silu(z_gate) * z_up.
+// bias and s are optional (NULL = 0 and 1).
+// ---------------------------------------------------------------------------
+#ifndef SWIGLU_BS_ROWS_PER_GROUP
+#define SWIGLU_BS_ROWS_PER_GROUP 128   // rows reduced in registers per block (backward)
+#endif
+#ifndef SWIGLU_BS_INTERLEAVE
+#define SWIGLU_BS_INTERLEAVE 1         // group y takes rows y, y+G, y+2G, ... (else a band)
+#endif
+constexpr int kBsRows = SWIGLU_BS_ROWS_PER_GROUP;
+constexpr int kWaves = kBlock / 64;
+
+// Exact sum of two fp32 values as head + tail (Knuth's two-sum).
+__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
+    s = a + b;
+    const float bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+
+template <typename T, int VEC, bool WIDE>
+__global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
+    const T* __restrict__ gp, int64_t gs, const T* __restrict__ up, int64_t us,
+    T* __restrict__ y, int64_t ys, const T* __restrict__ bg, const T* __restrict__ bu,
+    const float* __restrict__ sc, int64_t scs, Geom G) {
+    int64_t row;
+    uint32_t col;
+    if (!locate<WIDE>(G, row, col)) return;
+    const int64_t c = (int64_t)col * VEC;
+    float g[VEC], u[VEC], out[VEC];
+    Vec<T, VEC>::load(gp + row * gs + c, g);
+    Vec<T, VEC>::load(up + row * us + c, u);
+    if (bg != nullptr) {
+        float b[VEC], d[VEC];
+        Vec<T, VEC>::template load<true>(bg + c, b);
+        Vec<T, VEC>::template load<true>(bu + c, d);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            g[i] += b[i];
+            u[i] += d[i];
+        }
+    }
+    const float s = sc != nullptr ? sc[row * scs] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+        float sig, osig;
+        sigmoid_pair<T, false>(g[i], sig, osig);
+        out[i] = ((g[i] * sig) * u[i]) * s;
+    }
+    Vec<T, VEC>::store(y + row * ys + c, out);
+}
+
+// Partial sums of a backward over rows [row0 + y*R, row0 + (y+1)*R) for the
+// column tile x. Writes dz for every element; part_db[group][k] gets this
+// group's column sums (k in [0, 2n): gate columns, then up columns) and
+// part_ds[row][x][w] wave w's share of each row's ds. Fixed summation order
+// throughout: each lane adds its rows in order, each wave's share is a fixed
+// butterfly, and the second pass adds tiles and waves in order.
+struct BsGeom {
+    int64_t rows;       // rows in this launch
+    int64_t n;          // half width (elements)
+    int64_t group0;     // global index of this launch's first row group
+    int64_t row0;       // global index of this launch's first row
+    uint32_t nv;        // vectors per half row
+    uint32_t tiles;     // column tiles per row (= gridDim.x)
+};
+
+// Sum of v over the 64 lanes of a wave, in a fixed order, through DPP lane
+// permutes (no LDS): pairs, quads, 8-lane and 16-lane mirrors, then the
+// row broadcasts that fold the four 16-lane rows into lane 63. Every lane
+// of the wave must be active. Returns the total (read from lane 63).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f<0x141, 0xF>(v);   // row_half_mirror
+    v += dpp_f<0x140, 0xF>(v);   // row_mirror
+    v += dpp_f<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_f<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+template <typename T, int VEC, bool IN_PLACE>
+__global__ __launch_bounds__(kBlock) void swiglu_bwd_bs_kernel(
+    const T* dyp, int64_t dys, T* gp, int64_t gs, T* up, int64_t us, T* dgp, int64_t dgs,
+    T* dup, int64_t dus, const T* __restrict__ bg, const T* __restrict__ bu,
+    const float* __restrict__ sc, int64_t scs, float* part_db, float* part_ds, BsGeom G) {
+    if constexpr (IN_PLACE) {
+        dgp = gp;
+        dgs = gs;
+        dup = up;
+        dus = us;
+    }
+    const uint32_t col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+    const bool active = col < G.nv;
+    const int64_t c = (int64_t)col * VEC;
+    // Rows of this group, in the order they are summed: with INTERLEAVE the
+    // G = gridDim.y groups advance through the tensor together (row
+    // blockIdx.y + j*G at step j), so the rows in flight across the grid form
+    // one contiguous band, as in a one-shot grid; otherwise group y owns the
+    // band [y*R, (y+1)*R).
+#if SWIGLU_BS_INTERLEAVE
+    const int64_t r_first = blockIdx.y, r_step = gridDim.y;
+#else
+    const int64_t r_first = (int64_t)blockIdx.y * kBsRows, r_step = 1;
+#endif
+    float bgv[VEC], buv[VEC], acc_g[VEC], acc_u[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+        bgv[i] = buv[i] = 0.0f;
+        acc_g[i] = acc_u[i] = 0.0f;
+    }
+    if (bg != nullptr && active) {
+        Vec<T, VEC>::template load<true>(bg + c, bgv);
+        Vec<T, VEC>::template load<true>(bu + c, buv);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int j = 0; j < kBsRows; ++j) {
+        const int64_t row = r_first + j * r_step;
+        if (row >= G.rows) break;                     // uniform
+        const float s = sc != nullptr ? sc[row * scs] : 1.0f;
+        float p = 0.0f;
+        if (active) {
+            float g[VEC], u[VEC], d[VEC], dg[VEC], du[VEC];
+            Vec<T, VEC>::load(gp + row * gs + c, g);
+            Vec<T, VEC>::load(up + row * us + c, u);
+            Vec<T, VEC>::load(dyp + row * dys + c, d);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                float zg, zlo;
+                two_sum(g[i], bgv[i], zg, zlo);
+                const float zu = u[i] + buv[i];
+                float sig, osig;
+                sigmoid_pair<T, true>(zg, sig, osig);
+                const float h = h_factor_lo<T>(zg, zlo, osig);
+                const float silu = zg * sig;
+                const float ds_ = d[i] * s;
+                du[i] = ds_ * silu;
+                dg[i] = ((ds_ * zu) * sig) * h;
+                p = __builtin_fmaf(d[i] * silu, zu, p);
+                acc_g[i] += dg[i];
+                acc_u[i] += du[i];
+            }
+            Vec<T, VEC>::store(dgp + row * dgs + c, dg);
+            Vec<T, VEC>::store(dup + row * dus + c, du);
+        }
+        if (part_ds != nullptr) {
+            // One partial per (row, tile, wave); the second pass adds the
+            // tiles and waves of a row in order.
+            const float w = wave_sum(p);
+            if (lane == 0) part_ds[((G.row0 + row) * G.tiles + blockIdx.x) * kWaves + wave] = w;
+        }
+    }
+    if (part_db != nullptr && active) {
+        float* pg = part_db + (G.group0 + blockIdx.y) * (2 * G.n) + c;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            pg[i] = acc_g[i];
+            pg[G.n + i] = acc_u[i];
+        }
+    }
+}
+
+// out[k * out_stride] = sum over j < count of part[j * jstride + k * kstride],
+// j in order, for k < width.
+__global__ __launch_bounds__(kBlock) void swiglu_sum_partials_kernel(
+    const float* __restrict__ part, int64_t count, int64_t jstride, int64_t kstride,
+    int64_t width, float* __restrict__ out, int64_t out_stride) {
+    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (k >= width) return;
+    const float* p = part + k * kstride;
+    float acc = 0.0f;
+    for (int64_t j = 0; j < count; ++j) acc += p[j * jstride];
+    out[k * out_stride] = acc;
+}
+
+__global__ __launch_bounds__(kBlock) void swiglu_zero_kernel(float* p, int64_t count,
+                                                             int64_t stride) {
+    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (k < count) p[k * stride] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+// ---- bias / scale variants ---------------------------------------------------
+struct BsArgs {
+    const void* bias;        // [2n] of T or NULL
+    const float* scale;      // [rows] with stride scale_stride, or NULL
+    int64_t scale_stride;
+};
+
+template <typename T, int VEC>
+swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, int64_t n,
+                            hipStream_t stream) {
+    const Plan P = make_plan(n, VEC);
+    const void* k = P.wide ? reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, true>)
+                           : reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, false>);
+    const T* g;
+    const T* u;
+    T* y;
+    int64_t gs = ops[0].stride, us = ops[1].stride, ys = ops[2].stride, scs = A.scale_stride;
+    const T* bg = static_cast<const T*>(A.bias);
+    const T* bu = bg != nullptr ? bg + n : nullptr;
+    const float* sc;
+    Geom G;
+    G.nv = P.nv;
+    G.rpb = P.rpb;
+    G.inv_nv = 1.0f / (float)P.nv;
+    void* args[] = {&g, &gs, &u, &us, &y, &ys, &bg, &bu, &sc, &scs, &G};
+    for (int64_t r0 = 0; r0 < rows; r0 += P.rows_per_launch) {
+        const int64_t rc = rows - r0 < P.rows_per_launch ? rows - r0 : P.rows_per_launch;
+        g = static_cast<const T*>(ops[0].p) + r0 * gs;
+        u = static_cast<const T*>(ops[1].p) + r0 * us;
+        y = const_cast<T*>(static_cast<const T*>(ops[2].p)) + r0 * ys;
+        sc = A.scale != nullptr ? A.scale + r0 * scs : nullptr;
+        G.rows = rc;
+        const uint32_t groups = (uint32_t)((rc + P.rpb - 1) / P.rpb);
+        if (hipLaunchKernel(k, dim3(P.tiles, groups), dim3(kBlock), args, 0, stream) != hipSuccess)
+            return SWIGLU_ERR_HIP;
+    }
+    return SWIGLU_OK;
+}
+
+// Workspace layout of the backward: [part_db: groups x 2n fp32]
+// [part_ds: rows x tiles x waves fp32],
+// each part starting on a 256-byte boundary. tiles is bounded by the
+// single-element access width, so the size does not depend on alignment.
+int64_t bs_groups(int64_t rows) { return (rows + kBsRows - 1) / kBsRows; }
+int64_t bs_max_tiles(int64_t n) { return (n + kBlock - 1) / kBlock; }
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+size_t bs_workspace_bytes(int64_t rows, int64_t n, bool want_db, bool want_ds) {
+    int64_t b = 0;
+    if (want_db) b += round256(bs_groups(rows) * 2 * n * 4);
+    if (want_ds) b += round256(rows * bs_max_tiles(n) * kWaves * 4);
+    return (size_t)b;
+}
+
+swiglu_status zero_fill(float* p, int64_t count, int64_t stride, hipStream_t stream) {
+    if (count <= 0) return SWIGLU_OK;
+    void* args[] = {&p, &count, &stride};
+    const uint32_t blocks = (uint32_t)((count + kBlock - 1) / kBlock);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&swiglu_zero_kernel), dim3(blocks),
+                           dim3(kBlock), args, 0, stream) == hipSuccess
+               ? SWIGLU_OK
+               : SWIGLU_ERR_HIP;
+}
+
+swiglu_status sum_partials(const float* part, int64_t count, int64_t jstride, int64_t kstride,
+                           int64_t width, float* out, int64_t out_stride, hipStream_t stream) {
+    void* args[] = {&part, &count, &jstride, &kstride, &width, &out, &out_stride};
+    const uint32_t blocks = (uint32_t)((width + kBlock - 1) / kBlock);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&swiglu_sum_partials_kernel),
+                           dim3(blocks), dim3(kBlock), args, 0, stream) == hipSuccess
+               ? SWIGLU_OK
+               : SWIGLU_ERR_HIP;
+}
+
+// ops: dy, gate, up, dgate, dup.
+template <typename T, int VEC>
+swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, int64_t n,
+                            bool in_place, float* dbias, float* dscale, int64_t dscale_stride,
+                            void* workspace, hipStream_t stream) {
+    const uint32_t nv = (uint32_t)(n / VEC);
+    const uint32_t tiles = (nv + kBlock - 1) / kBlock;
+    const int64_t groups = bs_groups(rows);
+    float* part_db = nullptr;
+    float* part_ds = nullptr;
+    char* ws = static_cast<char*>(workspace);
+    if (dbias != nullptr) {
+        part_db = reinterpret_cast<float*>(ws);
+        ws += round256(groups * 2 * n * 4);
+    }
+    if (dscale != nullptr) part_ds = reinterpret_cast<float*>(ws);
+
+    const void* k = in_place ? reinterpret_cast<const void*>(&swiglu_bwd_bs_kernel<T, VEC, true>)
+                             : reinterpret_cast<const void*>(&swiglu_bwd_bs_kernel<T, VEC, false>);
+    const T *dyp, *bg = static_cast<const T*>(A.bias), *bu;
+    T *gp, *upp, *dgp, *dup;
+    int64_t dys = ops[0].stride, gs = ops[1].stride, us = ops[2].stride, dgs = ops[3].stride,
+            dus = ops[4].stride, scs = A.scale_stride;
+    bu = bg != nullptr ? bg + n : nullptr;
+    const float* sc;
+    BsGeom G;
+    G.n = n;
+    G.nv = nv;
+    G.tiles = tiles;
+    void* args[] = {&dyp, &dys, &gp, &gs, &upp, &us, &dgp, &dgs, &dup, &dus,
+                    &bg, &bu, &sc, &scs, &part_db, &part_ds, &G};
+    const int64_t rows_per_launch = (int64_t)kMaxGridY * kBsRows;
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+        const int64_t rc = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+        dyp = static_cast<const T*>(ops[0].p) + r0 * dys;
+        gp = const_cast<T*>(static_cast<const T*>(ops[1].p)) + r0 * gs;
+        upp = const_cast<T*>(static_cast<const T*>(ops[2].p)) + r0 * us;
+        dgp = const_cast<T*>(static_cast<const T*>(ops[3].p)) + r0 * dgs;
+        dup = const_cast<T*>(static_cast<const T*>(ops[4].p)) + r0 * dus;
+        sc = A.scale != nullptr ? A.scale + r0 * scs : nullptr;
+        G.rows = rc;
+        G.row0 = r0;
+        G.group0 = r0 / kBsRows;
+        const uint32_t gy = (uint32_t)bs_groups(rc);
+        if (hipLaunchKernel(k, dim3(tiles, gy), dim3(kBlock), args, 0, stream) != hipSuccess)
+            return SWIGLU_ERR_HIP;
+    }
+    swiglu_status st = SWIGLU_OK;
+    if (dbias != nullptr)
+        st = sum_partials(part_db, groups, 2 * n, 1, 2 * n, dbias, 1, stream);
+    if (st == SWIGLU_OK && dscale != nullptr)
+        st = sum_partials(part_ds, (int64_t)tiles * kWaves, 1, (int64_t)tiles * kWaves, rows,
+                          dscale, dscale_stride, stream);
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) size_t swiglu_gateup_bias_scale_workspace_size(
+    int64_t rows, int64_t n, int want_dbias, int want_dscale) {
+    if (rows <= 0 || n <= 0 || n > (int64_t)INT32_MAX) return 0;
+    return bs_workspace_bytes(rows, n, want_dbias != 0, want_dscale != 0);
+}
+
+__attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_fwd(
+    const void* x, int64_t x_row_stride, const void* bias, const float* scale,
+    int64_t scale_stride, void* y, int64_t y_row_stride, int64_t rows, int64_t n,
+    swiglu_dtype dtype, hipStream_t stream) {
+    swiglu_status st = check_shape(rows, n, dtype);
+    if (st != SWIGLU_OK) return st;
+    const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
+    if ((st = check_operand(rows, x_row_stride, 2 * n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, y_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if (scale != nullptr && (st = check_operand(rows, scale_stride, 1, 4)) != SWIGLU_OK) return st;
+    if (rows == 0 || n == 0) return SWIGLU_OK;
+    if (!x || !y) return SWIGLU_ERR_NULL_POINTER;
+    const Operand ox{x, x_row_stride}, oy{y, y_row_stride};
+    if (views_overlap(ox, 2 * n, oy, n, rows, esz)) return SWIGLU_ERR_ALIASING;
+    const swiglu_host::Span sy = swiglu_host::span_of(oy, rows, n, esz);
+    if (bias != nullptr &&
+        swiglu_host::spans_overlap(sy, swiglu_host::span_of(Operand{bias, 2 * n}, 1, 2 * n, esz)))
+        return SWIGLU_ERR_ALIASING;
+    if (scale != nullptr &&
+        swiglu_host::spans_overlap(sy, swiglu_host::span_of(Operand{scale, scale_stride}, rows, 1, 4)))
+        return SWIGLU_ERR_ALIASING;
+
+    const BsArgs A{bias, scale, scale_stride};
+    const Operand ops[5] = {ox, Operand{offset(x, n, esz), x_row_stride}, oy,
+                            Operand{bias, 0}, Operand{offset(bias, n, esz), 0}};
+    const int vb = vec_bytes((int)esz, ops, bias != nullptr ? 5 : 3);
+    if (dtype == SWIGLU_DTYPE_BF16) {
+        switch (vb) {
+            case 16: return fwd_bs_launch<uint16_t, 8>(ops, A, rows, n, stream);
+            case 8: return fwd_bs_launch<uint16_t, 4>(ops, A, rows, n, stream);
+            case 4: return fwd_bs_launch<uint16_t, 2>(ops, A, rows, n, stream);
+            default: return fwd_bs_launch<uint16_t, 1>(ops, A, rows, n, stream);
+        }
+    }
+    switch (vb) {
+        case 16: return fwd_bs_launch<float, 4>(ops, A, rows, n, stream);
+        case 8: return fwd_bs_launch<float, 2>(ops, A, rows, n, stream);
+        default: return fwd_bs_launch<float, 1>(ops, A, rows, n, stream);
+    }
+}
+
+__attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bwd(
+    const void* dy, int64_t dy_row_stride, void* x, int64_t x_row_stride, const void* bias,
+    const float* scale, int64_t scale_stride, void* dx, int64_t dx_row_stride, float* dbias,
+    float* dscale, int64_t dscale_stride, void* workspace, size_t workspace_bytes, int64_t rows,
+    int64_t n, swiglu_dtype dtype, int in_place, hipStream_t stream) {
+    swiglu_status st = check_shape(rows, n, dtype);
+    if (st != SWIGLU_OK) return st;
+    const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
+    const bool ip = in_place != 0;
+    if (ip) {
+        if (dx != nullptr && dx != x) return SWIGLU_ERR_ALIASING;
+        dx = x;
+        dx_row_stride = x_row_stride;
+    }
+    if ((st = check_operand(rows, dy_row_stride, n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, x_row_stride, 2 * n, esz)) != SWIGLU_OK) return st;
+    if ((st = check_operand(rows, dx_row_stride, 2 * n, esz)) != SWIGLU_OK) return st;
+    if (scale != nullptr && (st = check_operand(rows, scale_stride, 1, 4)) != SWIGLU_OK) return st;
+    if (dscale != nullptr && (st = check_operand(rows, dscale_stride, 1, 4)) != SWIGLU_OK) return st;
+    if ((dbias != nullptr && bias == nullptr) || (dscale != nullptr && scale == nullptr))
+        return SWIGLU_ERR_NULL_POINTER;
+    if (rows == 0 || n == 0) {
+        // Sums over nothing: dbias is 0 when there are no rows, each ds is 0
+        // when rows are empty of columns.
+        if (rows == 0 && n > 0 && dbias != nullptr) return zero_fill(dbias, 2 * n, 1, stream);
+        if (n == 0 && rows > 0 && dscale != nullptr)
+            return zero_fill(dscale, rows, dscale_stride, stream);
+        return SWIGLU_OK;
+    }
+    if (!dy || !x || !dx) return SWIGLU_ERR_NULL_POINTER;
+    const size_t need = bs_workspace_bytes(rows, n, dbias != nullptr, dscale != nullptr);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || (uintptr_t)workspace % 16))
+        return SWIGLU_ERR_WORKSPACE;
+
+    const Operand ody{dy, dy_row_stride}, ox{x, x_row_stride}, odx{dx, dx_row_stride};
+    if (views_overlap(ody, n, ox, 2 * n, rows, esz)) return SWIGLU_ERR_ALIASING;
+    if (!ip && (views_overlap(odx, 2 * n, ox, 2 * n, rows, esz) ||
+                views_overlap(odx, 2 * n, ody, n, rows, esz)))
+        return SWIGLU_ERR_ALIASING;
+    // Every other pair: outputs (dx, dbias, dscale, workspace) against
+    // everything else, by memory span.
+    using swiglu_host::Span;
+    using swiglu_host::span_of;
+    using swiglu_host::spans_overlap;
+    Span ins[4];
+    int nin = 0;
+    ins[nin++] = span_of(ody, rows, n, esz);
+    if (!ip) ins[nin++] = span_of(ox, rows, 2 * n, esz);
+    if (bias != nullptr) ins[nin++] = span_of(Operand{bias, 2 * n}, 1, 2 * n, esz);
+    if (scale != nullptr) ins[nin++] = span_of(Operand{scale, scale_stride}, rows, 1, 4);
+    Span outs[4];
+    int nout = 0;
+    outs[nout++] = span_of(odx, rows, 2 * n, esz);
+    if (dbias != nullptr) outs[nout++] = span_of(Operand{dbias, 2 * n}, 1, 2 * n, 4);
+    if (dscale != nullptr) outs[nout++] = span_of(Operand{dscale, dscale_stride}, rows, 1, 4);
+    if (need > 0) outs[nout++] = Span{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    for (int i = 0; i < nout; ++i) {
+        for (int j = (i == 0 ? 2 - (ip ? 1 : 0) : 0); j < nin; ++j)   // dx vs dy/x: checked above
+            if (spans_overlap(outs[i], ins[j])) return SWIGLU_ERR_ALIASING;
+        for (int j = i + 1; j < nout; ++j)
+            if (spans_overlap(outs[i], outs[j])) return SWIGLU_ERR_ALIASING;
+    }
+
+    const BsArgs A{bias, scale, scale_stride};
+    const Operand ops[7] = {ody, ox, Operand{offset(x, n, esz), x_row_stride}, odx,
+                            Operand{offset(dx, n, esz), dx_row_stride}, Operand{bias, 0},
+                            Operand{offset(bias, n, esz), 0}};
+    const int vb = vec_bytes((int)esz, ops, bias != nullptr ? 7 : 5);
+#define SWIGLU_BWD_BS(T, V)                                                                  \
+    bwd_bs_launch<T, V>(ops, A, rows, n, ip, dbias, dscale, dscale_stride, workspace, stream)
+    if (dtype == SWIGLU_DTYPE_BF16) {
+        switch (vb) {
+            case 16: return SWIGLU_BWD_BS(uint16_t, 8);
+            case 8: return SWIGLU_BWD_BS(uint16_t, 4);
+            case 4: return SWIGLU_BWD_BS(uint16_t, 2);
+            default: return SWIGLU_BWD_BS(uint16_t, 1);
+        }
+    }
+    switch (vb) {
+        case 16: return SWIGLU_BWD_BS(float, 4);
+        case 8: return SWIGLU_BWD_BS(float, 2);
+        default: return SWIGLU_BWD_BS(float, 1);
+    }
+#undef SWIGLU_BWD_BS
+}
+
+}  // extern "C"

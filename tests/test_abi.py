@@ -160,7 +160,7 @@ def _hex_const(src: str, name: str) -> float:
 def test_kernel_constants_match_their_definitions():
     """The fp32 constants in the kernel source equal the splits of log2(e),
     ln 2, g0 = -1 - W(1/e) and e^{g0}, derived here at 50 digits."""
-    src = open(os.path.join(ROOT, "swiglu_activation_amd", "csrc", "swiglu_gateup.hip")).read()
+    src = open(os.path.join(ROOT, "swiglu_activation_amd", "csrc", "swiglu_device.h")).read()
     with mpmath.workdps(50):
         l2e = 1 / mpmath.log(2)
         g0 = -1 - mpmath.lambertw(1 / mpmath.e).real
@@ -193,9 +193,9 @@ def test_bias_scale_workspace_size(lib):
     assert ws(0, 32768, 1, 1) == 0 and ws(8, 0, 1, 1) == 0 and ws(-1, 8, 1, 1) == 0
     groups = (8192 + 127) // 128
     assert ws(8192, 32768, 1, 0) == r256(groups * 2 * 32768 * 4)
-    assert ws(8192, 32768, 0, 1) == r256(8192 * 128 * 4)
-    assert ws(8192, 32768, 1, 1) == r256(groups * 2 * 32768 * 4) + r256(8192 * 128 * 4)
-    assert ws(300, 1001, 1, 1) == r256(3 * 2002 * 4) + r256(300 * 4 * 4)
+    assert ws(8192, 32768, 0, 1) == r256(8192 * 128 * 4 * 4)
+    assert ws(8192, 32768, 1, 1) == r256(groups * 2 * 32768 * 4) + r256(8192 * 128 * 4 * 4)
+    assert ws(300, 1001, 1, 1) == r256(3 * 2002 * 4) + r256(300 * 4 * 4 * 4)
 
 
 @no_gpu_only
