@@ -17,6 +17,8 @@ from .swiglu import (  # noqa: F401
     bf16_ulp_distance,
     oracle_bwd,
     oracle_bwd_bias_scale,
+    oracle_fc1,
+    oracle_fc1_swiglu,
     oracle_fwd,
     oracle_fwd_bias_scale,
     round_f64_to_bf16_bits,

@@ -169,6 +169,31 @@ def oracle_bwd_bias_scale(x, dy, bias=None, scale=None):
 
 
 # --------------------------------------------------------------------------
+# fc1 projection with the SwiGLU as its epilogue
+# --------------------------------------------------------------------------
+# Liger-Kernel Megatron SwiGLU page, §Background: the packed [tokens, 2n]
+# tensor is the output of one fc1 projection (Megatron's ColumnParallelLinear).
+# Its weight W is [2n, hidden] in the Linear layout (row j holds output column
+# j's weights), so x = A @ W.T, with the gate columns from rows [0, n) of W and
+# the up columns from rows [n, 2n). The fused variant computes
+#     y = silu(A @ W[:n].T) * (A @ W[n:].T)
+# without forming x (the "MLP1 with activation" of the Liger-Kernel test/cute
+# page, §MLP1 numerical reference). Products of the inputs are exact in
+# float64 for bf16 inputs; the sums are numpy's float64 matmul.
+
+def oracle_fc1(a, w) -> np.ndarray:
+    """x = A @ W.T in float64: A [m, k], W [2n, k] -> [m, 2n]."""
+    a = np.asarray(a, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    return a @ w.T
+
+
+def oracle_fc1_swiglu(a, w) -> np.ndarray:
+    """y = silu(A @ W[:n].T) * (A @ W[n:].T), float64 [m, n]."""
+    return oracle_fwd(oracle_fc1(a, w))
+
+
+# --------------------------------------------------------------------------
 # Comparison targets
 # --------------------------------------------------------------------------
 

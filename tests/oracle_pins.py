@@ -174,3 +174,40 @@ def pin_bias_scale_finite_differences(impl):
 
 
 BIAS_SCALE_PINS = [pin_bias_scale_reduces_to_base, pin_bias_scale_finite_differences]
+
+
+def pin_fc1_matmul_bruteforce(impl):
+    """x = A @ W.T against a triple loop on a tiny case (exact integers)."""
+    rng = np.random.default_rng(51)
+    a = rng.integers(-4, 5, (3, 5)).astype(float)
+    w = rng.integers(-4, 5, (4, 5)).astype(float)
+    x = impl.oracle_fc1(a, w)
+    for i in range(3):
+        for j in range(4):
+            assert x[i, j] == sum(a[i, k] * w[j, k] for k in range(5))
+
+
+def pin_fc1_swiglu_identity(impl):
+    """With A = I the projection returns W.T, so the fused op is the base
+    forward on the packed W.T; gate rows of W come first."""
+    rng = np.random.default_rng(52)
+    k, n = 6, 3
+    w = rng.standard_normal((2 * n, k))
+    y = impl.oracle_fc1_swiglu(np.eye(k), w)
+    assert np.array_equal(y, impl.oracle_fwd(w.T))
+    # swapping the gate and up halves of W changes the result
+    assert not np.allclose(y, impl.oracle_fc1_swiglu(np.eye(k), np.concatenate([w[n:], w[:n]])))
+
+
+def pin_fc1_swiglu_linear_in_up(impl):
+    """y is linear in the up weights and in A's scale on the up side only
+    through silu: doubling W_up doubles y."""
+    rng = np.random.default_rng(53)
+    a = rng.standard_normal((4, 8))
+    w = rng.standard_normal((6, 8))
+    w2 = w.copy()
+    w2[3:] *= 2.0
+    assert np.allclose(impl.oracle_fc1_swiglu(a, w2), 2.0 * impl.oracle_fc1_swiglu(a, w), rtol=1e-14)
+
+
+FC1_PINS = [pin_fc1_matmul_bruteforce, pin_fc1_swiglu_identity, pin_fc1_swiglu_linear_in_up]

@@ -23,7 +23,8 @@ def _impl(**over):
     base = dict(sigmoid=oracle.sigmoid, silu=oracle.silu, silu_grad=oracle.silu_grad,
                 oracle_fwd=oracle.oracle_fwd, oracle_bwd=oracle.oracle_bwd,
                 oracle_fwd_bias_scale=oracle.oracle_fwd_bias_scale,
-                oracle_bwd_bias_scale=oracle.oracle_bwd_bias_scale)
+                oracle_bwd_bias_scale=oracle.oracle_bwd_bias_scale,
+                oracle_fc1=oracle.oracle_fc1, oracle_fc1_swiglu=oracle.oracle_fc1_swiglu)
     base.update(over)
     return types.SimpleNamespace(**base)
 
@@ -39,7 +40,8 @@ def _tiny_inputs():
 # The oracle passes every pin
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.BIAS_SCALE_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.BIAS_SCALE_PINS + pins.FC1_PINS,
+                         ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(_impl())
 
@@ -175,6 +177,29 @@ def test_planted_bias_scale_mistake_is_caught(name):
             with np.errstate(all="ignore"):
                 pin(impl)
         except AssertionError:
+            caught += 1
+    assert caught >= 1, f"mutant {name} passed every pin"
+
+
+FC1_MUTANTS = {
+    "fc1_reshape_for_transpose": dict(oracle_fc1=lambda a, w: np.asarray(a, float) @ np.asarray(
+        w, float).reshape(np.asarray(w).shape[1], np.asarray(w).shape[0])),
+    "fc1_halves_swapped": dict(oracle_fc1_swiglu=lambda a, w: oracle.oracle_fwd(
+        oracle.oracle_fc1(a, np.concatenate([np.asarray(w)[np.asarray(w).shape[0] // 2:],
+                                             np.asarray(w)[:np.asarray(w).shape[0] // 2]])))),
+    "fc1_sum_off_by_one": dict(oracle_fc1=lambda a, w: np.asarray(a, float)[:, 1:] @ np.asarray(w, float)[:, 1:].T),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FC1_MUTANTS))
+def test_planted_fc1_mistake_is_caught(name):
+    impl = _impl(**FC1_MUTANTS[name])
+    caught = 0
+    for pin in pins.FC1_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl)
+        except (AssertionError, TypeError, ValueError):
             caught += 1
     assert caught >= 1, f"mutant {name} passed every pin"
 
