@@ -89,6 +89,55 @@ def cpu_baseline(w, x_h, dy_h, seconds: float):
                       "widen to float64, forward, backward (numpy, one thread)"}
 
 
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+
+
+def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768))):
+    """fc1 projection with the SwiGLU epilogue (one kernel) against
+    torch.matmul (hipBLASLt) followed by the elementwise SwiGLU, for
+    (hidden, n) pairs at the given token count; 2 m k 2n FLOPs."""
+    import numpy as np
+    import torch
+
+    import swiglu_activation_amd as sw
+    out = {}
+    for hidden, n in shapes:
+        gen = torch.Generator(device=dev).manual_seed(hidden + n)
+        a = torch.randn(tokens, hidden, device=dev, generator=gen).bfloat16()
+        wt = (torch.randn(2 * n, hidden, device=dev, generator=gen) / hidden ** 0.5).bfloat16()
+        y = torch.empty(tokens, n, dtype=torch.bfloat16, device=dev)
+        xbuf = torch.empty(tokens, 2 * n, dtype=torch.bfloat16, device=dev)
+        flops = 2.0 * tokens * hidden * 2 * n
+
+        def timed(fn, iters=10):
+            ts = []
+            for k in range(iters + 2):
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                fn()
+                s1.record(stream)
+                s1.synchronize()
+                if k >= 2:
+                    ts.append(s0.elapsed_time(s1))
+            return float(np.mean(ts))
+
+        fused = timed(lambda: sw.swiglu_fc1_fwd(a, wt, y))
+        fused_x = timed(lambda: sw.swiglu_fc1_fwd(a, wt, y, x_out=xbuf))
+        mm = timed(lambda: torch.matmul(a, wt.t(), out=xbuf))
+        unfused = timed(lambda: (torch.matmul(a, wt.t(), out=xbuf), sw.swiglu_gateup_fwd(xbuf, y)))
+        out[f"tokens{tokens}_hidden{hidden}_n{n}"] = {
+            "fused_ms": round(fused, 4), "fused_TFLOPs": round(flops / fused / 1e9, 1),
+            "fused_frac_of_peak": round(flops / fused / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "fused_with_x_ms": round(fused_x, 4),
+            "hipblaslt_matmul_ms": round(mm, 4),
+            "hipblaslt_TFLOPs": round(flops / mm / 1e9, 1),
+            "matmul_then_swiglu_ms": round(unfused, 4)}
+        log(f"[bench] fc1 h={hidden} n={n}: fused {fused:.3f} ms ({flops / fused / 1e9:.0f} TFLOP/s), "
+            f"matmul {mm:.3f} ms, matmul+swiglu {unfused:.3f} ms")
+        del a, wt, y, xbuf
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +339,7 @@ def main():
                                         "dscale (GB/s on the base op's bytes)"}
         log(f"[bench] bias+scale fwd {bf:.4f} ms, bwd {bb:.4f} ms")
         del ws
+        passes["fc1_swiglu"] = fc1_leg(dev, stream, w.rows)
         if (w.n * e) % 16 == 0 and w.rows <= 65535:
             # The same access patterns with no arithmetic: the best this memory
             # system streams for each mix, on the same buffers and grid.

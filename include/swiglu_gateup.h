@@ -237,6 +237,38 @@ swiglu_status swiglu_gateup_bias_scale_bwd(const void* dy, int64_t dy_row_stride
                                            int64_t rows, int64_t n,
                                            swiglu_dtype dtype, int in_place, hipStream_t stream);
 
+/*
+ * fc1 projection with the SwiGLU as its epilogue (Liger-Kernel Megatron
+ * SwiGLU page, §Background: the packed [tokens, 2n] tensor is the output of
+ * one fc1 projection; Liger-Kernel test/cute page, §MLP1 numerical reference:
+ * fused MLP1-with-activation variants). With W = [Wg; Wu] of shape [2n, k] in
+ * the Linear layout (row j holds output feature j),
+ *     y = silu(A Wg^T) * (A Wu^T)            ([m, n])
+ * is computed without writing the [m, 2n] product, which stays in fp32
+ * registers (bf16 inputs, fp32 accumulation on the matrix cores, one
+ * nearest-even rounding of y). On request the product itself is also
+ * written, rounded to bf16, for a later backward.
+ *
+ *   a, lda        [m, k] activations (tokens), row stride lda (elements).
+ *   w, ldw        [2n, k] weights: rows [0, n) gate, [n, 2n) up; stride ldw.
+ *   y, ldy        [m, n] output, row stride ldy.
+ *   x_out, ldx    NULL, or [m, 2n] output receiving A W^T (bf16), stride ldx.
+ *   m, n, k       sizes: m >= 0; n >= 0 and a multiple of 64; k a positive
+ *                 multiple of 64 (k may be 0 only when m or n is 0).
+ *   dtype         must be SWIGLU_DTYPE_BF16.
+ * All pointers must be 16-byte aligned and all row strides multiples of 8.
+ *
+ * Errors: SWIGLU_ERR_BAD_DTYPE (not bf16), SWIGLU_ERR_BAD_SHAPE (n or k not
+ * multiples of 64, k == 0 with a non-empty output), SWIGLU_ERR_BAD_STRIDE
+ * (strides below the widths, misaligned pointers or strides),
+ * SWIGLU_ERR_NULL_POINTER, SWIGLU_ERR_ALIASING (an output overlaps an input
+ * or the other output), SWIGLU_ERR_HIP.
+ */
+swiglu_status swiglu_fc1_fwd(const void* a, int64_t lda, const void* w, int64_t ldw,
+                             void* y, int64_t ldy, void* x_out, int64_t ldx,
+                             int64_t m, int64_t n, int64_t k,
+                             swiglu_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* swiglu_status_string(swiglu_status status);
 

@@ -18,7 +18,7 @@ import os
 
 __all__ = ["swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
            "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
-           "swiglu_gateup_bias_scale_workspace_size", "swiglu_status_string",
+           "swiglu_gateup_bias_scale_workspace_size", "swiglu_fc1_fwd", "swiglu_status_string",
            "SwiGLUError", "library_path", "load_library", "EXPORTS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +39,7 @@ _BAD_DTYPE_CODE = -1    # passed for any other torch dtype; the library rejects 
 
 EXPORTS = ("swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
            "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
-           "swiglu_gateup_bias_scale_workspace_size", "swiglu_status_string")
+           "swiglu_gateup_bias_scale_workspace_size", "swiglu_fc1_fwd", "swiglu_status_string")
 
 _lib = None
 
@@ -87,6 +87,8 @@ def load_library():
     lib.swiglu_gateup_bias_scale_bwd.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp,
                                                  i64, vp, ctypes.c_size_t, i64, i64, cint, cint, vp]
     lib.swiglu_gateup_bias_scale_bwd.restype = cint
+    lib.swiglu_fc1_fwd.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, cint, vp]
+    lib.swiglu_fc1_fwd.restype = cint
     lib.swiglu_status_string.argtypes = [cint]
     lib.swiglu_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -422,3 +424,41 @@ def swiglu_gateup_bias_scale_bwd(dy, x, bias=None, scale=None, dx=None, *, want_
             _dtype_code(x), 1 if in_place else 0, _stream_handle(x.device, stream))
     _check(st, "swiglu_gateup_bias_scale_bwd")
     return out, dbias, dscale
+
+
+# ---------------------------------------------------------------------------
+# fc1 projection with the SwiGLU epilogue
+# ---------------------------------------------------------------------------
+
+def swiglu_fc1_fwd(a, w, y=None, *, x_out=None, stream=None):
+    """y = silu(a @ w[:n].T) * (a @ w[n:].T) for bf16 a [..., k] and w [2n, k].
+
+    x_out: None, True (allocate) or a [..., 2n] tensor that receives a @ w.T.
+    Returns y, or (y, x_out) when x_out is requested."""
+    import torch
+    lib = load_library()
+    _require_device(a, w, y, x_out if isinstance(x_out, torch.Tensor) else None)
+    if w.dim() != 2 or w.shape[0] % 2:
+        raise ValueError("w must be [2n, k]")
+    n, k = w.shape[0] // 2, w.shape[1]
+    if a.shape[-1] != k:
+        raise ValueError(f"a must have {k} columns")
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("swiglu_fc1_fwd needs bfloat16 a and w")
+    m, lda = _rows_and_stride(a, "a")
+    _, ldw = _rows_and_stride(w, "w")
+    if y is None:
+        y = torch.empty(tuple(a.shape[:-1]) + (n,), dtype=a.dtype, device=a.device)
+    ldy = _same_rows(y, m, n, "y")
+    want_x = x_out is not None and x_out is not False
+    if x_out is True:
+        x_out = torch.empty(tuple(a.shape[:-1]) + (2 * n,), dtype=a.dtype, device=a.device)
+    xp, ldx = None, 0
+    if want_x:
+        ldx = _same_rows(x_out, m, 2 * n, "x_out")
+        xp = x_out.data_ptr()
+    with torch.cuda.device(a.device):
+        st = lib.swiglu_fc1_fwd(a.data_ptr(), lda, w.data_ptr(), ldw, y.data_ptr(), ldy, xp, ldx,
+                                m, n, k, _dtype_code(a), _stream_handle(a.device, stream))
+    _check(st, "swiglu_fc1_fwd")
+    return (y, x_out) if want_x else y

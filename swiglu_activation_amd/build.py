@@ -15,7 +15,8 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 SRCS = [os.path.join(PKG_DIR, "csrc", "swiglu_gateup.hip"),
-        os.path.join(PKG_DIR, "csrc", "swiglu_bias_scale.hip")]
+        os.path.join(PKG_DIR, "csrc", "swiglu_bias_scale.hip"),
+        os.path.join(PKG_DIR, "csrc", "swiglu_fc1.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libswiglu_gateup.so")
 ARCH = "gfx950"

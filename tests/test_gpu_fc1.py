@@ -1,0 +1,113 @@
+"""fc1 projection with the SwiGLU epilogue vs the oracle (needs an MI355X).
+
+Bar. Inputs are bf16, products exact in fp32, sums accumulated in fp32 by
+the matrix cores in an unspecified order, so each accumulator D obeys
+|D - D_exact| <= E = k * 2^-24 * (|A| |W|^T) (the float64 sum of magnitudes).
+The epilogue then forms silu(g) u in fp32 and rounds once to bf16, so
+    |y - y_ref| <= 2 ulp_bf16(y_ref) + |silu'(g)| |u| E_g + |silu(g)| E_u
+(+ |E_g E_u| terms far below these), where g, u are the exact products. The
+product written to x_out obeys |x - x_ref| <= 1 ulp_bf16(x_ref) + E.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swiglu_activation_amd as sw
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_ulp(v):
+    """Spacing of the bf16 grid at |v| (subnormal spacing below 2^-126)."""
+    a = np.abs(v)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def _case(m, n, k, seed, scale_a=1.0):
+    rng = np.random.default_rng(seed)
+    a = oracle.round_f64_to_bf16_bits(rng.standard_normal((m, k)) * scale_a)
+    w = oracle.round_f64_to_bf16_bits(rng.standard_normal((2 * n, k)) / np.sqrt(k))
+    return a, w
+
+
+def _check(a_h, w_h, y, x=None):
+    af, wf = oracle.widen(a_h, "bf16"), oracle.widen(w_h, "bf16")
+    n, k = wf.shape[0] // 2, wf.shape[1]
+    xref = oracle.oracle_fc1(af, wf)
+    yref = oracle.oracle_fwd(xref)
+    E = k * 2.0 ** -24 * (np.abs(af) @ np.abs(wf).T)
+    g, u = xref[:, :n], xref[:, n:]
+    s = oracle.sigmoid(g)
+    bound = (2 * _bf16_ulp(yref) + np.abs(oracle.silu_grad(g)) * np.abs(u) * E[:, :n]
+             + np.abs(g * s) * E[:, n:] + E[:, :n] * E[:, n:])
+    got = oracle.bf16_bits_to_f64(gu.from_dev(y))
+    err = np.abs(got - yref)
+    worst = float(np.max(err / bound))
+    print(f"    y: {yref.size} elements, worst {worst:.3g} of the bar", flush=True)
+    assert np.all(err <= bound), worst
+    if x is not None:
+        gx = oracle.bf16_bits_to_f64(gu.from_dev(x))
+        bx = _bf16_ulp(xref) + E
+        wx = float(np.max(np.abs(gx - xref) / bx))
+        print(f"    x: {xref.size} elements, worst {wx:.3g} of the bar", flush=True)
+        assert np.all(np.abs(gx - xref) <= bx), wx
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 256, 512), (300, 192, 320),
+                                   (1, 64, 64), (1000, 1792, 1024), (4096, 512, 4096)])
+def test_fc1_swiglu_parity(m, n, k):
+    """Ragged token counts (300, 1, 1000), a feature count that leaves a
+    half-empty 128-wide tile (192, 1792), and long k."""
+    print(f"[fc1] m={m} n={n} k={k}", flush=True)
+    a_h, w_h = _case(m, n, k, seed=m + n + k)
+    a, w = gu.to_dev(a_h, "bf16"), gu.to_dev(w_h, "bf16")
+    y, x = sw.swiglu_fc1_fwd(a, w, x_out=True)
+    torch.cuda.synchronize()
+    _check(a_h, w_h, y, x)
+    # the product written for the backward feeds the elementwise kernel to the same y
+    y2 = sw.swiglu_gateup_fwd(x)
+    torch.cuda.synchronize()
+    assert y2.shape == y.shape
+
+
+def test_fc1_swiglu_3d_input_and_strided_output():
+    a_h, w_h = _case(2 * 96, 256, 256, seed=7)
+    a = gu.to_dev(a_h, "bf16").reshape(2, 96, 256)
+    w = gu.to_dev(w_h, "bf16")
+    yb = torch.full((2 * 96, 256 + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = yb[:, :256]
+    sw.swiglu_fc1_fwd(a.reshape(192, 256), w, y)
+    y3 = sw.swiglu_fc1_fwd(a, w)
+    torch.cuda.synchronize()
+    assert y3.shape == (2, 96, 256)
+    assert gu.bits_equal(y3.reshape(192, 256), y)
+    assert torch.isnan(yb[:, 256:]).all()
+    _check(a_h, w_h, y)
+
+
+def test_fc1_deterministic():
+    a_h, w_h = _case(512, 512, 1024, seed=8)
+    a, w = gu.to_dev(a_h, "bf16"), gu.to_dev(w_h, "bf16")
+    y1 = sw.swiglu_fc1_fwd(a, w)
+    y2 = sw.swiglu_fc1_fwd(a, w)
+    torch.cuda.synchronize()
+    assert gu.bits_equal(y1, y2)
+
+
+def test_fc1_argument_errors():
+    a = torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(128, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        sw.swiglu_fc1_fwd(a.float(), w.float())                          # bf16 only
+    with pytest.raises(ValueError):
+        sw.swiglu_fc1_fwd(a[:, :32], w[:, :32])                          # k not a multiple of 64
+    with pytest.raises(ValueError):
+        sw.swiglu_fc1_fwd(a, torch.zeros(96, 64, dtype=torch.bfloat16, device="cuda"))  # n = 48
+    with pytest.raises(ValueError):
+        sw.swiglu_fc1_fwd(a, w, a[:, :64])                               # y overlaps a
