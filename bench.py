@@ -92,7 +92,7 @@ def cpu_baseline(w, x_h, dy_h, seconds: float):
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 
 
-def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768))):
+def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iters: int = 10):
     """fc1 projection with the SwiGLU epilogue (one kernel) against
     torch.matmul (hipBLASLt) followed by the elementwise SwiGLU, for
     (hidden, n) pairs at the given token count; 2 m k 2n FLOPs."""
@@ -109,7 +109,7 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768))):
         xbuf = torch.empty(tokens, 2 * n, dtype=torch.bfloat16, device=dev)
         flops = 2.0 * tokens * hidden * 2 * n
 
-        def timed(fn, iters=10):
+        def timed(fn):
             ts = []
             for k in range(iters + 2):
                 s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -149,6 +149,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the fwd+bwd step (for profiling runs)")
+    ap.add_argument("--fc1-only", action="store_true",
+                    help="time only the fc1 projection with the SwiGLU epilogue, print its "
+                         "figures as one JSON line, and exit (for profiling runs)")
     ap.add_argument("--calib", action="store_true",
                     help="also run plain 1 GiB copies (torch copy_ and an elementwise "
                          "negation) as the byte-counter calibration for rocprofv3 --pmc")
@@ -177,6 +180,10 @@ def main():
     w = synth.WORKLOADS[args.workload or synth.HEADLINE]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.fc1_only:
+        res = fc1_leg(dev, torch.cuda.current_stream(dev), w.rows, iters=args.steps)
+        print(json.dumps({"fc1_swiglu": res}), flush=True)
+        return
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     log(f"[bench] workload {w.name}: x {w.shape} {w.dtype}; drawing inputs")
     x_h, dy_h = synth.make_x(w), synth.make_dy(w)

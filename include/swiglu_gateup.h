@@ -253,8 +253,9 @@ swiglu_status swiglu_gateup_bias_scale_bwd(const void* dy, int64_t dy_row_stride
  *   w, ldw        [2n, k] weights: rows [0, n) gate, [n, 2n) up; stride ldw.
  *   y, ldy        [m, n] output, row stride ldy.
  *   x_out, ldx    NULL, or [m, 2n] output receiving A W^T (bf16), stride ldx.
- *   m, n, k       sizes: m >= 0; n >= 0 and a multiple of 64; k a positive
- *                 multiple of 64 (k may be 0 only when m or n is 0).
+ *   m, n, k       sizes: m >= 0; n a multiple of 64 in [0, 2^30]; k a
+ *                 positive multiple of 64 below 2^31 (k may be 0 only when m
+ *                 or n is 0).
  *   dtype         must be SWIGLU_DTYPE_BF16.
  * All pointers must be 16-byte aligned and all row strides multiples of 8.
  *

@@ -295,7 +295,9 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
     const void* a, int64_t lda, const void* w, int64_t ldw, void* y, int64_t ldy, void* x_out,
     int64_t ldx, int64_t m, int64_t n, int64_t k, swiglu_dtype dtype, hipStream_t stream) {
     if (dtype != SWIGLU_DTYPE_BF16) return SWIGLU_ERR_BAD_DTYPE;
-    if (m < 0 || n < 0 || k < 0 || n > (int64_t)INT32_MAX || k > (int64_t)INT32_MAX)
+    // 2n weight rows and k fit in 31 bits, so the feature-tile count fits
+    // one launch dimension with room to spare
+    if (m < 0 || n < 0 || k < 0 || n > ((int64_t)1 << 30) || k > (int64_t)INT32_MAX)
         return SWIGLU_ERR_BAD_SHAPE;
     if (n % 64 != 0 || k % kFcTileK != 0) return SWIGLU_ERR_BAD_SHAPE;
     swiglu_status st;
@@ -334,7 +336,12 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
     P.n = n;
     P.k = k;
     const uint32_t f_tiles = (uint32_t)((n + kFcTileF - 1) / kFcTileF);
-    const int64_t rows_per_launch = (int64_t)kMaxGridY * kFcTileT;
+    // One launch covers at most 2^24 - 1 workgroups (its work-item count must
+    // stay below 2^32) and 65535 token tiles.
+    const int64_t max_wg = ((int64_t)1 << 24) - 1;
+    int64_t tiles_per_launch = max_wg / f_tiles;
+    if (tiles_per_launch > kMaxGridY) tiles_per_launch = kMaxGridY;
+    const int64_t rows_per_launch = tiles_per_launch * kFcTileT;
     uint32_t t_tiles = 0;
     void* args[] = {&P, const_cast<uint32_t*>(&f_tiles), &t_tiles};
     for (int64_t r0 = 0; r0 < m; r0 += rows_per_launch) {

@@ -226,3 +226,55 @@ def test_bias_scale_validation(lib):
     # dscale stride below 1
     assert bsb(lib, A, 8, B, 16, None, bias, 1, C, 16, None, D, 0, D + 8192, 1 << 20, 4, 8) == \
         sw.SWIGLU_ERR_BAD_STRIDE
+
+
+def fc1(lib, a, lda, w, ldw, y, ldy, x, ldx, m, n, k, dt=BF16):
+    return lib.swiglu_fc1_fwd(a, lda, w, ldw, y, ldy, x, ldx, m, n, k, dt, None)
+
+
+@no_gpu_only
+def test_fc1_validation(lib):
+    D = 0x2100000
+    ok = dict(a=A, lda=64, w=B, ldw=64, y=C, ldy=128, x=None, ldx=0, m=4, n=128, k=64)
+
+    def call(**kw):
+        args = {**ok, **kw}
+        return fc1(lib, args["a"], args["lda"], args["w"], args["ldw"], args["y"], args["ldy"],
+                   args["x"], args["ldx"], args["m"], args["n"], args["k"], kw.get("dt", BF16))
+
+    assert call(dt=F32) == sw.SWIGLU_ERR_BAD_DTYPE
+    # shapes: n and k multiples of 64, n <= 2^30, nothing negative
+    assert call(n=96) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert call(k=32, lda=32, ldw=32) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert call(m=-1) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert call(n=(1 << 30) + 64, ldy=(1 << 30) + 64) == sw.SWIGLU_ERR_BAD_SHAPE
+    assert call(k=0, lda=0, ldw=0) == sw.SWIGLU_ERR_BAD_SHAPE        # an empty sum
+    # strides below the widths
+    assert call(lda=56) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(ldw=56) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(ldy=120) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(x=D, ldx=248) == sw.SWIGLU_ERR_BAD_STRIDE
+    # 16-byte pointers and strides that are multiples of 8 elements
+    assert call(lda=68) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(ldy=132) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(a=A + 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(y=C + 2) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(x=D + 4, ldx=256) == sw.SWIGLU_ERR_BAD_STRIDE
+    # NULL inputs or output
+    assert call(a=None) == sw.SWIGLU_ERR_NULL_POINTER
+    assert call(w=None) == sw.SWIGLU_ERR_NULL_POINTER
+    assert call(y=None) == sw.SWIGLU_ERR_NULL_POINTER
+    # outputs overlapping inputs or each other (a spans 4 * 64 * 2 = 512 bytes,
+    # w 256 * 64 * 2 = 32 KiB, y 4 * 128 * 2 bytes)
+    assert call(y=A + 256) == sw.SWIGLU_ERR_ALIASING
+    assert call(y=B + 16384) == sw.SWIGLU_ERR_ALIASING
+    assert call(x=A, ldx=256) == sw.SWIGLU_ERR_ALIASING
+    assert call(x=B + 4096, ldx=256) == sw.SWIGLU_ERR_ALIASING
+    assert call(x=C + 512, ldx=256) == sw.SWIGLU_ERR_ALIASING
+
+
+@no_gpu_only
+def test_fc1_empty_problems_launch_nothing(lib):
+    assert fc1(lib, None, 64, None, 64, None, 128, None, 0, 0, 128, 64) == sw.SWIGLU_OK
+    assert fc1(lib, None, 64, None, 64, None, 0, None, 0, 5, 0, 64) == sw.SWIGLU_OK
+    assert fc1(lib, None, 0, None, 0, None, 128, None, 0, 0, 128, 0) == sw.SWIGLU_OK
