@@ -17,12 +17,24 @@
 //    4 x 2 for the up projection (256 fp32 accumulators per lane, in the
 //    accumulation registers). Per 16-wide k step a wave reads 8 fragments
 //    from LDS for 16 MFMAs: 1/64 byte of LDS traffic per flop.
-//  * k is walked in 64-wide tiles through a double-buffered LDS stage
-//    (A: 256 x 64, W: 256 x 64 bf16, rows padded by 16 bytes, 144 KiB);
-//    the next tile's global loads are in flight while the current one feeds
-//    the MFMAs, the next k step's fragments are read while the current
-//    step's MFMAs run, and one barrier per tile separates the stages.
-//  * Rows past m (tokens) or n (features) load zeros and store nothing.
+//  * k is walked in 32-wide tiles through a ring of 4 LDS stages (each 256
+//    token rows + 256 weight rows of 64 bytes, 32 KiB). Global memory is
+//    copied straight into LDS (global_load_lds_dwordx4: no registers, no
+//    LDS write instructions); the copies of the next three tiles are in
+//    flight while one tile feeds the MFMAs, which covers the latency of an
+//    L2 miss. Each stage is its own LDS array and the loop is unrolled over
+//    the ring, so the compiler can tell the stage being read from the ones
+//    being filled and waits only where the data is needed.
+//  * A copy instruction writes 1 KiB of LDS in lane order (16 rows of 64
+//    bytes), so the layout is chosen through the global addresses: the
+//    16-byte chunk c of row r sits in slot c ^ ((r / 4) % 4) of its row,
+//    which makes the fragment reads free of bank conflicts.
+//  * The next k step's fragments are read while the current step's MFMAs
+//    run; one barrier per tile hands a filled stage to the readers and an
+//    emptied one to the copies.
+//  * Rows past m (tokens) or n (features) are clamped to the last valid row:
+//    they copy real data, which reaches only accumulators that are never
+//    stored.
 #include "swiglu_device.h"
 
 namespace {
@@ -31,48 +43,42 @@ using namespace swiglu_impl;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef SWIGLU_FC_WAVE_T
-#define SWIGLU_FC_WAVE_T 128    // tokens per wave (multiple of 32)
-#endif
-#ifndef SWIGLU_FC_WAVE_F
-#define SWIGLU_FC_WAVE_F 64     // output features per wave (multiple of 32)
-#endif
-#ifndef SWIGLU_FC_WAVES_T
-#define SWIGLU_FC_WAVES_T 2     // waves along tokens
-#endif
-#ifndef SWIGLU_FC_WAVES_F
-#define SWIGLU_FC_WAVES_F 2     // waves along features
-#endif
-#ifndef SWIGLU_FC_TILE_K
-#define SWIGLU_FC_TILE_K 64     // k per LDS stage
-#endif
 #ifndef SWIGLU_FC_GROUP
-#define SWIGLU_FC_GROUP 16      // token tiles that share a weight tile in the launch order
+#define SWIGLU_FC_GROUP 32      // token tiles that share a weight tile in the launch order
 #endif
-#ifndef SWIGLU_FC_SPLIT_STORE
-#define SWIGLU_FC_SPLIT_STORE 0 // write the next stage to LDS between k steps
+#ifndef SWIGLU_FC_XCD
+#define SWIGLU_FC_XCD 0         // give each XCD a contiguous range of the launch order
 #endif
-#ifndef SWIGLU_FC_FRAG_DB
-#define SWIGLU_FC_FRAG_DB 1     // read the next k step's fragments during the MFMAs
+#ifndef SWIGLU_FC_SCHED
+#define SWIGLU_FC_SCHED 1       // pin the interleaving of MFMAs and memory instructions
 #endif
 
-constexpr int kFcMT = SWIGLU_FC_WAVE_T / 32;         // 32x32 tiles per wave along tokens
-constexpr int kFcMF = SWIGLU_FC_WAVE_F / 32;         // ... along features (each: gate + up)
-constexpr int kFcThreads = 64 * SWIGLU_FC_WAVES_T * SWIGLU_FC_WAVES_F;
-constexpr int kFcTileT = SWIGLU_FC_WAVE_T * SWIGLU_FC_WAVES_T;   // tokens per workgroup
-constexpr int kFcTileF = SWIGLU_FC_WAVE_F * SWIGLU_FC_WAVES_F;   // features per workgroup
-constexpr int kFcTileK = SWIGLU_FC_TILE_K;
-constexpr int kFcPitch = kFcTileK + 8;               // LDS row pitch in bf16 (16-byte pad)
+constexpr int kFcWaveT = 128;                        // tokens per wave
+constexpr int kFcWaveF = 64;                         // features per wave (gate and up each)
+constexpr int kFcWavesT = 2, kFcWavesF = 2;
+constexpr int kFcWaves = kFcWavesT * kFcWavesF;
+constexpr int kFcThreads = 64 * kFcWaves;
+constexpr int kFcMT = kFcWaveT / 32;                 // 32x32 tiles per wave along tokens
+constexpr int kFcMF = kFcWaveF / 32;                 // ... along features (each: gate + up)
+constexpr int kFcTileT = kFcWaveT * kFcWavesT;       // tokens per workgroup
+constexpr int kFcTileF = kFcWaveF * kFcWavesF;       // features per workgroup
+constexpr int kFcTileK = 32;                         // k per stage
+constexpr int kFcStages = 4;
 constexpr int kFcRowsA = kFcTileT;                   // token rows per stage
-constexpr int kFcRowsW = 2 * kFcTileF;               // gate rows, then up rows
-constexpr int kFcStage = (kFcRowsA + kFcRowsW) * kFcPitch;   // bf16 per stage
-constexpr int kFcVecRow = kFcTileK / 8;              // 16-byte vectors per row
-constexpr int kFcVecA = kFcRowsA * kFcVecRow / kFcThreads;
-constexpr int kFcVecW = kFcRowsW * kFcVecRow / kFcThreads;
-static_assert(kFcVecA * kFcThreads == kFcRowsA * kFcVecRow, "A tile split");
-static_assert(kFcVecW * kFcThreads == kFcRowsW * kFcVecRow, "W tile split");
-static_assert(2 * kFcStage * 2 <= 160 * 1024, "two stages must fit in LDS");
+constexpr int kFcRows = kFcTileT + 2 * kFcTileF;     // + gate rows + up rows
+constexpr int kFcRowElems = kFcTileK;                // bf16 per LDS row (no padding)
+constexpr int kFcStageElems = kFcRows * kFcRowElems;
+constexpr int kFcChunks = kFcTileK / 8;              // 16-byte chunks per row
+constexpr int kFcCopyRows = 64 / kFcChunks;          // rows per copy instruction (one wave)
+constexpr int kFcCopies = kFcRows / kFcCopyRows / kFcWaves;   // copies per thread per tile
+constexpr int kFcMfma = 2 * kFcMF * kFcMT;           // MFMAs per wave per k step
+constexpr int kFcReads = kFcMT + 2 * kFcMF;          // fragment reads per k step
+static_assert(kFcTileK == 32 && kFcChunks == 4, "two 16-wide k steps per tile, 4 chunks per row");
+static_assert(kFcCopies * kFcWaves * kFcCopyRows == kFcRows, "whole copies per stage");
+static_assert(kFcRowsA % kFcCopyRows == 0 && kFcTileF % kFcCopyRows == 0, "copies do not straddle");
+static_assert(kFcStages * kFcStageElems * 2 <= 160 * 1024, "the ring must fit in LDS");
 
 struct Fc1Args {
     const uint16_t* a;   // [m, k] tokens, row stride lda
@@ -83,70 +89,81 @@ struct Fc1Args {
     int64_t m, n, k;
 };
 
-// Global -> registers for one stage. Thread t loads, for vector v, row
-// (v * threads + t) / kFcVecRow and 16-byte column t % kFcVecRow of the A
-// tile and of the W tile (gate rows, then up rows).
-struct Stage {
-    u32x4 a[kFcVecA];
-    u32x4 w[kFcVecW];
+// The LDS ring: one array per stage.
+__shared__ __attribute__((aligned(16))) uint16_t fc_stage0[kFcStageElems];
+__shared__ __attribute__((aligned(16))) uint16_t fc_stage1[kFcStageElems];
+__shared__ __attribute__((aligned(16))) uint16_t fc_stage2[kFcStageElems];
+__shared__ __attribute__((aligned(16))) uint16_t fc_stage3[kFcStageElems];
+
+template <int S>
+__device__ __forceinline__ uint16_t* stage() {
+    static_assert(S >= 0 && S < kFcStages, "stage index");
+    if constexpr (S == 0) return fc_stage0;
+    else if constexpr (S == 1) return fc_stage1;
+    else if constexpr (S == 2) return fc_stage2;
+    else return fc_stage3;
+}
+
+// Slot of 16-byte chunk c in LDS row r.
+__device__ __forceinline__ int chunk_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// Source row of each of this thread's copies, at k = 0. Copy i of wave v
+// fills LDS rows [16 q, 16 q + 16) of a stage, q = i * waves + v; lane l
+// writes slot l % 4 of row 16 q + l / 4, so it reads the chunk that belongs
+// in that slot.
+struct Sources {
+    const uint16_t* p[kFcCopies];
 };
 
-__device__ __forceinline__ void load_stage(const Fc1Args& P, int64_t t0, int64_t f0, int64_t k0,
-                                           Stage& s) {
-    const int t = threadIdx.x;
-    const int cv = t % kFcVecRow;
+__device__ __forceinline__ void make_sources(const Fc1Args& P, int64_t t0, int64_t f0,
+                                             Sources& src) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int v = 0; v < kFcVecA; ++v) {
-        const int r = (v * kFcThreads + t) / kFcVecRow;
-        const int64_t tok = t0 + r;
-        if (tok < P.m)
-            s.a[v] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(P.a + tok * P.lda + k0 + cv * 8));
-        else
-            s.a[v] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int v = 0; v < kFcVecW; ++v) {
-        const int r = (v * kFcThreads + t) / kFcVecRow;
-        const int64_t f = f0 + (r % kFcTileF);
-        const int64_t wrow = (r < kFcTileF ? 0 : P.n) + f;
-        if (f < P.n)
-            s.w[v] = *reinterpret_cast<const u32x4*>(P.w + wrow * P.ldw + k0 + cv * 8);
-        else
-            s.w[v] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kFcCopies; ++i) {
+        const int r = (i * kFcWaves + wave) * kFcCopyRows + lane / kFcChunks;
+        const int c = chunk_slot(r, lane % kFcChunks);
+        if (r < kFcRowsA) {
+            const int64_t tok = t0 + r < P.m ? t0 + r : P.m - 1;
+            src.p[i] = P.a + tok * P.lda + c * 8;
+        } else {
+            const int wr = r - kFcRowsA;                       // gate rows, then up rows
+            const int64_t f = f0 + (wr % kFcTileF) < P.n ? f0 + (wr % kFcTileF) : P.n - 1;
+            src.p[i] = P.w + ((wr < kFcTileF ? 0 : P.n) + f) * P.ldw + c * 8;
+        }
     }
 }
 
-// Writes part `part` of `parts` of the staged vectors to LDS.
-template <int PART, int PARTS>
-__device__ __forceinline__ void store_stage_part(uint16_t* lds, const Stage& s) {
-    const int t = threadIdx.x;
-    const int cv = t % kFcVecRow;
-    uint16_t* la = lds;
-    uint16_t* lw = lds + kFcRowsA * kFcPitch;
-    constexpr int nA = kFcVecA / PARTS, nW = kFcVecW / PARTS;
-    static_assert(nA * PARTS == kFcVecA && nW * PARTS == kFcVecW, "even split");
-#pragma unroll
-    for (int v = PART * nA; v < (PART + 1) * nA; ++v) {
-        const int r = (v * kFcThreads + t) / kFcVecRow;
-        *reinterpret_cast<u32x4*>(la + r * kFcPitch + cv * 8) = s.a[v];
-    }
-#pragma unroll
-    for (int v = PART * nW; v < (PART + 1) * nW; ++v) {
-        const int r = (v * kFcThreads + t) / kFcVecRow;
-        *reinterpret_cast<u32x4*>(lw + r * kFcPitch + cv * 8) = s.w[v];
-    }
-}
-
-__device__ __forceinline__ void store_stage(uint16_t* lds, const Stage& s) {
-    store_stage_part<0, 1>(lds, s);
-}
-
-// Store part s of the next stage after k step s (all parts by the last step).
+// Starts the copies of k tile t into stage S.
 template <int S>
-__device__ __forceinline__ void store_after_step(uint16_t* lds, const Stage& st) {
-    constexpr int steps = kFcTileK / 16;
-    store_stage_part<S, steps>(lds, st);
+__device__ __forceinline__ void copy_tile(const Sources& src, int t) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kFcCopies; ++i) {
+        uint16_t* dst = stage<S>() + (i * kFcWaves + wave) * kFcCopyRows * kFcRowElems;
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(src.p[i] + (int64_t)t * kFcTileK),
+            (lds_void*)(dst), 16, 0, 0);
+    }
+}
+
+// s_waitcnt: at most N copies (vector memory operations) outstanding, and
+// no LDS operation.
+template <int N>
+__device__ __forceinline__ void wait_copies_and_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // vmcnt in bits [3:0] and [15:14], expcnt (7: not waited on) in [6:4],
+    // lgkmcnt (0) in [11:8]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier for the ring. The caller has waited for its own LDS
+// reads and for the copies the next stage needs (s_waitcnt); the empty asm
+// statements keep the compiler from moving memory accesses across the
+// barrier. A fence here would drain every copy in flight.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
@@ -158,15 +175,61 @@ struct Frags {
     bf16x8 a[kFcMT], g[kFcMF], u[kFcMF];
 };
 
-__device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* lw, int wt, int wf,
-                                           int frow, int kk, Frags& F) {
+// off: this lane's element offset for the step (its row within a 32-row
+// tile, and the swizzled slot of its chunk).
+template <int S>
+__device__ __forceinline__ void load_frags(int wt, int wf, int off, Frags& F) {
+    const uint16_t* base = stage<S>();
 #pragma unroll
-    for (int j = 0; j < kFcMT; ++j) F.a[j] = frag(la + (wt + 32 * j + frow) * kFcPitch + kk);
+    for (int j = 0; j < kFcMT; ++j) F.a[j] = frag(base + (wt + 32 * j) * kFcRowElems + off);
 #pragma unroll
     for (int i = 0; i < kFcMF; ++i) {
-        F.g[i] = frag(lw + (wf + 32 * i + frow) * kFcPitch + kk);
-        F.u[i] = frag(lw + (kFcTileF + wf + 32 * i + frow) * kFcPitch + kk);
+        F.g[i] = frag(base + (kFcRowsA + wf + 32 * i) * kFcRowElems + off);
+        F.u[i] = frag(base + (kFcRowsA + kFcTileF + wf + 32 * i) * kFcRowElems + off);
     }
+}
+
+struct Acc {
+    f32x16 g[kFcMF][kFcMT], u[kFcMF][kFcMT];   // [feature tile][token tile]
+};
+
+__device__ __forceinline__ void mfma_step(const Frags& C, Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < kFcMF; ++i)
+#pragma unroll
+        for (int j = 0; j < kFcMT; ++j) {
+            acc.g[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(C.g[i], C.a[j], acc.g[i][j], 0, 0, 0);
+            acc.u[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(C.u[i], C.a[j], acc.u[i][j], 0, 0, 0);
+        }
+}
+
+// Scheduling hints (instruction classes of the AMDGPU scheduler).
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+
+__device__ __forceinline__ void sched_reads_among_mfma() {
+#if SWIGLU_FC_SCHED
+#pragma unroll
+    for (int q = 0; q < kFcReads; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, kFcMfma - kFcReads, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+__device__ __forceinline__ void sched_copies_reads_among_mfma() {
+#if SWIGLU_FC_SCHED
+    static_assert(kFcCopies == kFcReads, "one copy and one read per MFMA pair below");
+#pragma unroll
+    for (int q = 0; q < kFcReads; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, kFcMfma - kFcReads, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#endif
 }
 
 // Launch order of the output tiles: consecutive workgroups take GROUP token
@@ -176,6 +239,13 @@ __device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* l
 // Infinity Cache.
 __device__ __forceinline__ void tile_of(uint32_t b, uint32_t f_tiles, uint32_t t_tiles,
                                         uint32_t& ft, uint32_t& tt) {
+#if SWIGLU_FC_XCD
+    // Workgroups are dealt to the 8 XCDs round robin; renumber them so that
+    // each XCD walks a contiguous range of the order above.
+    const uint32_t total = f_tiles * t_tiles, q = total / 8, r = total % 8;
+    const uint32_t xcd = b % 8, idx = b / 8;
+    b = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+#endif
     const uint32_t per_group = SWIGLU_FC_GROUP * f_tiles;
     const uint32_t g = b / per_group, in = b % per_group;
     const uint32_t first_t = g * SWIGLU_FC_GROUP;
@@ -184,77 +254,104 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t f_tiles, uint32_t t
     ft = in / gs;
 }
 
+struct Ctx {
+    Sources src;
+    int wt, wf, off0, off1;
+    int kt_count;   // k tiles
+    int pad;        // leading padding tiles that round the count up to the ring size
+};
+
+// Source tile of ring slot kt: padding slots and slots past the end are
+// clamped to a real tile (their copies land in stages whose data is never
+// multiplied in).
+__device__ __forceinline__ int source_tile(const Ctx& c, int kt) {
+    const int t = kt - c.pad;
+    return t < 0 ? 0 : t < c.kt_count ? t : c.kt_count - 1;
+}
+
+// The fragments with the token operand zeroed when `live` is false, so a
+// padding tile adds nothing.
+__device__ __forceinline__ Frags masked(const Frags& F, bool live) {
+    Frags r = F;
+#pragma unroll
+    for (int j = 0; j < kFcMT; ++j) r.a[j] = live ? F.a[j] : bf16x8{};
+    return r;
+}
+
+// Ring slot kt (tile kt - pad), held in stage S = kt % 4. Entering: F0
+// holds (or is receiving) the slot's first-step fragments, and the copies of
+// slots kt + 1 .. kt + 3 are in flight or done. The first step's MFMAs run
+// while the second step's fragments are read. Then: wait for slot kt + 1,
+// barrier (slot kt + 1 is complete for every wave, and stage S has been read
+// by every wave), start the copies of slot kt + 4 into stage S and read slot
+// kt + 1's first-step fragments while the second step's MFMAs run. After the
+// last slot these extra copies and reads are not used.
+template <int S>
+__device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
+    constexpr int SN = (S + 1) % kFcStages;
+    const bool live = kt >= c.pad;
+    load_frags<S>(c.wt, c.wf, c.off1, F1);
+    mfma_step(masked(F0, live), acc);
+    sched_reads_among_mfma();
+    wait_copies_and_lds<2 * kFcCopies>();              // slots kt + 2 and kt + 3 may be pending
+    ring_barrier();
+    copy_tile<S>(c.src, source_tile(c, kt + kFcStages));
+    load_frags<SN>(c.wt, c.wf, c.off0, F0);
+    mfma_step(masked(F1, live), acc);
+    sched_copies_reads_among_mfma();
+}
+
 __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint32_t f_tiles,
                                                                 uint32_t t_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kFcStage];   // 2 stages
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wf = (wave % SWIGLU_FC_WAVES_F) * SWIGLU_FC_WAVE_F;   // wave's feature offset
-    const int wt = (wave / SWIGLU_FC_WAVES_F) * SWIGLU_FC_WAVE_T;   // wave's token offset
     uint32_t ft, tt;
     tile_of(blockIdx.x, f_tiles, t_tiles, ft, tt);
     const int64_t f0 = (int64_t)ft * kFcTileF;
     const int64_t t0 = (int64_t)tt * kFcTileT;
 
-    f32x16 acc_g[kFcMF][kFcMT], acc_u[kFcMF][kFcMT];   // [feature tile][token tile]
+    Acc acc;
 #pragma unroll
     for (int i = 0; i < kFcMF; ++i)
 #pragma unroll
         for (int j = 0; j < kFcMT; ++j) {
-            acc_g[i][j] = f32x16{};
-            acc_u[i][j] = f32x16{};
+            acc.g[i][j] = f32x16{};
+            acc.u[i][j] = f32x16{};
         }
 
-    const int kt_count = (int)(P.k / kFcTileK);
-    Stage st;
-    load_stage(P, t0, f0, 0, st);
-    store_stage(lds, st);
-    __syncthreads();
-
-    const int frow = lane % 32;                    // fragment row within a 32-tile
-    const int fk = 8 * (lane / 32);                // fragment k offset within a 16-step
-    for (int kt = 0; kt < kt_count; ++kt) {
-        if (kt + 1 < kt_count) load_stage(P, t0, f0, (int64_t)(kt + 1) * kFcTileK, st);
-        const uint16_t* la = lds + (kt & 1) * kFcStage;
-        const uint16_t* lw = la + kFcRowsA * kFcPitch;
-#if SWIGLU_FC_FRAG_DB
-        // Fragments for step s + 1 are read while the MFMAs of step s run.
-        Frags F[2];
-        load_frags(la, lw, wt, wf, frow, fk, F[0]);
-#endif
-#pragma unroll
-        for (int s = 0; s < kFcTileK / 16; ++s) {
-#if SWIGLU_FC_FRAG_DB
-            if (s + 1 < kFcTileK / 16)
-                load_frags(la, lw, wt, wf, frow, 16 * (s + 1) + fk, F[(s + 1) & 1]);
-            const Frags& C = F[s & 1];
-#else
-            Frags C;
-            load_frags(la, lw, wt, wf, frow, 16 * s + fk, C);
-#endif
-#pragma unroll
-            for (int i = 0; i < kFcMF; ++i)
-#pragma unroll
-                for (int j = 0; j < kFcMT; ++j) {
-                    acc_g[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(C.g[i], C.a[j],
-                                                                        acc_g[i][j], 0, 0, 0);
-                    acc_u[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(C.u[i], C.a[j],
-                                                                        acc_u[i][j], 0, 0, 0);
-                }
-#if SWIGLU_FC_SPLIT_STORE
-            if (kt + 1 < kt_count) {
-                uint16_t* nxt = lds + ((kt + 1) & 1) * kFcStage;
-                if (s == 0) store_after_step<0>(nxt, st);
-                if constexpr (kFcTileK / 16 > 1) if (s == 1) store_after_step<1>(nxt, st);
-                if constexpr (kFcTileK / 16 > 2) if (s == 2) store_after_step<2>(nxt, st);
-                if constexpr (kFcTileK / 16 > 3) if (s == 3) store_after_step<3>(nxt, st);
-            }
-#endif
-        }
-#if !SWIGLU_FC_SPLIT_STORE
-        if (kt + 1 < kt_count) store_stage(lds + ((kt + 1) & 1) * kFcStage, st);
-#endif
-        __syncthreads();
+    Ctx c;
+    make_sources(P, t0, f0, c.src);
+    c.wf = (wave % kFcWavesF) * kFcWaveF;            // wave's feature offset
+    c.wt = (wave / kFcWavesF) * kFcWaveT;            // wave's token offset
+    c.kt_count = (int)(P.k / kFcTileK);
+    const int slots = (c.kt_count + kFcStages - 1) / kFcStages * kFcStages;
+    c.pad = slots - c.kt_count;
+    {
+        // A fragment lane reads row lane % 32 of a 32-row tile and chunk
+        // 2 s + lane / 32 in step s.
+        const int frow = lane % 32;
+        c.off0 = frow * kFcRowElems + chunk_slot(frow, lane / 32) * 8;
+        c.off1 = frow * kFcRowElems + chunk_slot(frow, 2 + lane / 32) * 8;
     }
+
+    // Fill the ring and wait for slot 0.
+    copy_tile<0>(c.src, source_tile(c, 0));
+    copy_tile<1>(c.src, source_tile(c, 1));
+    copy_tile<2>(c.src, source_tile(c, 2));
+    copy_tile<3>(c.src, source_tile(c, 3));
+    wait_copies_and_lds<3 * kFcCopies>();
+    ring_barrier();
+    Frags F0, F1;
+    load_frags<0>(c.wt, c.wf, c.off0, F0);
+
+    // unrolled over the ring so that every stage is named statically
+    for (int kt = 0; kt < slots; kt += kFcStages) {
+        k_tile<0>(c, kt, F0, F1, acc);
+        k_tile<1>(c, kt + 1, F0, F1, acc);
+        k_tile<2>(c, kt + 2, F0, F1, acc);
+        k_tile<3>(c, kt + 3, F0, F1, acc);
+    }
+    // No copy may still be writing LDS when the workgroup ends.
+    wait_copies_and_lds<0>();
 
     // Epilogue. Register v of a 32x32 tile holds feature
     // (v % 4) + 8 (v / 4) + 4 (lane / 32) and token lane % 32, so each group
@@ -263,17 +360,17 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     for (int i = 0; i < kFcMF; ++i)
 #pragma unroll
         for (int j = 0; j < kFcMT; ++j) {
-            const int64_t tok = t0 + wt + 32 * j + lane % 32;
+            const int64_t tok = t0 + c.wt + 32 * j + lane % 32;
             if (tok >= P.m) continue;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t f = f0 + wf + 32 * i + 8 * q + 4 * (lane / 32);
+                const int64_t f = f0 + c.wf + 32 * i + 8 * q + 4 * (lane / 32);
                 if (f >= P.n) continue;                 // n is a multiple of 64
                 float yv[4], gv[4], uv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    gv[r] = acc_g[i][j][4 * q + r];
-                    uv[r] = acc_u[i][j][4 * q + r];
+                    gv[r] = acc.g[i][j][4 * q + r];
+                    uv[r] = acc.u[i][j][4 * q + r];
                     float sig, osig;
                     sigmoid_pair<uint16_t, false>(gv[r], sig, osig);
                     yv[r] = (gv[r] * sig) * uv[r];
@@ -299,7 +396,7 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
     // one launch dimension with room to spare
     if (m < 0 || n < 0 || k < 0 || n > ((int64_t)1 << 30) || k > (int64_t)INT32_MAX)
         return SWIGLU_ERR_BAD_SHAPE;
-    if (n % 64 != 0 || k % kFcTileK != 0) return SWIGLU_ERR_BAD_SHAPE;
+    if (n % 64 != 0 || k % 64 != 0) return SWIGLU_ERR_BAD_SHAPE;
     swiglu_status st;
     if ((st = check_operand(m, lda, k, 2)) != SWIGLU_OK) return st;
     if ((st = check_operand(2 * n, ldw, k, 2)) != SWIGLU_OK) return st;
