@@ -17,18 +17,20 @@
 //    4 x 2 for the up projection (256 fp32 accumulators per lane, in the
 //    accumulation registers). Per 16-wide k step a wave reads 8 fragments
 //    from LDS for 16 MFMAs: 1/64 byte of LDS traffic per flop.
-//  * k is walked in 32-wide tiles through a ring of 4 LDS stages (each 256
-//    token rows + 256 weight rows of 64 bytes, 32 KiB). Global memory is
-//    copied straight into LDS (global_load_lds_dwordx4: no registers, no
-//    LDS write instructions); the copies of the next three tiles are in
-//    flight while one tile feeds the MFMAs, which covers the latency of an
-//    L2 miss. Each stage is its own LDS array and the loop is unrolled over
-//    the ring, so the compiler can tell the stage being read from the ones
-//    being filled and waits only where the data is needed.
-//  * A copy instruction writes 1 KiB of LDS in lane order (16 rows of 64
-//    bytes), so the layout is chosen through the global addresses: the
-//    16-byte chunk c of row r sits in slot c ^ ((r / 4) % 4) of its row,
-//    which makes the fragment reads free of bank conflicts.
+//  * k is walked in tiles of TILE_K (64) through a ring of STAGES (2) LDS
+//    stages, each 256 token rows + 256 weight rows of TILE_K bf16. Global
+//    memory is copied straight into LDS (global_load_lds_dwordx4: no
+//    registers, no LDS write instructions); the copies of the next
+//    STAGES - 1 tiles are in flight while one tile feeds the MFMAs. Each
+//    stage is its own LDS array and the loop is unrolled over the ring, so
+//    the compiler can tell the stage being read from the ones being filled
+//    and waits only where the data is needed. (64-wide tiles in 2 stages
+//    measured faster than 32-wide tiles in 3 to 5: each copy instruction
+//    then reads whole 128-byte lines.)
+//  * A copy instruction writes 1 KiB of LDS in lane order (rows of
+//    2 TILE_K bytes), so the layout is chosen through the global addresses:
+//    the 16-byte chunks of a row are permuted by an XOR with bits of the
+//    row index, which makes the fragment reads free of bank conflicts.
 //  * The next k step's fragments are read while the current step's MFMAs
 //    run; one barrier per tile hands a filled stage to the readers and an
 //    emptied one to the copies.
@@ -64,8 +66,14 @@ constexpr int kFcMT = kFcWaveT / 32;                 // 32x32 tiles per wave alo
 constexpr int kFcMF = kFcWaveF / 32;                 // ... along features (each: gate + up)
 constexpr int kFcTileT = kFcWaveT * kFcWavesT;       // tokens per workgroup
 constexpr int kFcTileF = kFcWaveF * kFcWavesF;       // features per workgroup
-constexpr int kFcTileK = 32;                         // k per stage
-constexpr int kFcStages = 4;
+#ifndef SWIGLU_FC_TILE_K
+#define SWIGLU_FC_TILE_K 64     // k per stage (32 or 64)
+#endif
+constexpr int kFcTileK = SWIGLU_FC_TILE_K;           // k per stage
+#ifndef SWIGLU_FC_STAGES
+#define SWIGLU_FC_STAGES 2      // LDS stages in the ring (2 to 5; x k per stage <= 160 KiB)
+#endif
+constexpr int kFcStages = SWIGLU_FC_STAGES;
 constexpr int kFcRowsA = kFcTileT;                   // token rows per stage
 constexpr int kFcRows = kFcTileT + 2 * kFcTileF;     // + gate rows + up rows
 constexpr int kFcRowElems = kFcTileK;                // bf16 per LDS row (no padding)
@@ -75,7 +83,9 @@ constexpr int kFcCopyRows = 64 / kFcChunks;          // rows per copy instructio
 constexpr int kFcCopies = kFcRows / kFcCopyRows / kFcWaves;   // copies per thread per tile
 constexpr int kFcMfma = 2 * kFcMF * kFcMT;           // MFMAs per wave per k step
 constexpr int kFcReads = kFcMT + 2 * kFcMF;          // fragment reads per k step
-static_assert(kFcTileK == 32 && kFcChunks == 4, "two 16-wide k steps per tile, 4 chunks per row");
+constexpr int kFcSteps = kFcTileK / 16;              // MFMA k steps per stage
+static_assert(kFcTileK == 32 || kFcTileK == 64, "4 or 8 chunks per row");
+static_assert(kFcSteps % 2 == 0, "fragment sets alternate within a stage");
 static_assert(kFcCopies * kFcWaves * kFcCopyRows == kFcRows, "whole copies per stage");
 static_assert(kFcRowsA % kFcCopyRows == 0 && kFcTileF % kFcCopyRows == 0, "copies do not straddle");
 static_assert(kFcStages * kFcStageElems * 2 <= 160 * 1024, "the ring must fit in LDS");
@@ -90,10 +100,14 @@ struct Fc1Args {
 };
 
 // The LDS ring: one array per stage.
+static_assert(kFcStages >= 2 && kFcStages <= 5, "ring size");
 __shared__ __attribute__((aligned(16))) uint16_t fc_stage0[kFcStageElems];
 __shared__ __attribute__((aligned(16))) uint16_t fc_stage1[kFcStageElems];
 __shared__ __attribute__((aligned(16))) uint16_t fc_stage2[kFcStageElems];
 __shared__ __attribute__((aligned(16))) uint16_t fc_stage3[kFcStageElems];
+#if SWIGLU_FC_STAGES == 5
+__shared__ __attribute__((aligned(16))) uint16_t fc_stage4[kFcStageElems];
+#endif
 
 template <int S>
 __device__ __forceinline__ uint16_t* stage() {
@@ -101,11 +115,19 @@ __device__ __forceinline__ uint16_t* stage() {
     if constexpr (S == 0) return fc_stage0;
     else if constexpr (S == 1) return fc_stage1;
     else if constexpr (S == 2) return fc_stage2;
-    else return fc_stage3;
+    else if constexpr (S == 3) return fc_stage3;
+#if SWIGLU_FC_STAGES == 5
+    else return fc_stage4;
+#endif
 }
 
-// Slot of 16-byte chunk c in LDS row r.
-__device__ __forceinline__ int chunk_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
+// Slot of 16-byte chunk c in LDS row r. A fragment read takes one chunk
+// from each of 16 consecutive rows per LDS cycle; the swizzle spreads them
+// over all 64 banks.
+__device__ __forceinline__ int chunk_slot(int r, int c) {
+    if constexpr (kFcChunks == 4) return c ^ ((r >> 2) & 3);
+    else return c ^ ((r >> 1) & 7);
+}
 
 // Source row of each of this thread's copies, at k = 0. Copy i of wave v
 // fills LDS rows [16 q, 16 q + 16) of a stage, q = i * waves + v; lane l
@@ -220,10 +242,11 @@ __device__ __forceinline__ void sched_reads_among_mfma() {
 
 __device__ __forceinline__ void sched_copies_reads_among_mfma() {
 #if SWIGLU_FC_SCHED
-    static_assert(kFcCopies == kFcReads, "one copy and one read per MFMA pair below");
+    constexpr int per = kFcCopies / kFcReads;        // copies per fragment read
+    static_assert(per * kFcReads == kFcCopies, "copies spread evenly over the reads");
 #pragma unroll
     for (int q = 0; q < kFcReads; ++q) {
-        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, per, 0);
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
@@ -256,7 +279,8 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t f_tiles, uint32_t t
 
 struct Ctx {
     Sources src;
-    int wt, wf, off0, off1;
+    int wt, wf;
+    int off[kFcSteps];   // this lane's fragment offset in each k step
     int kt_count;   // k tiles
     int pad;        // leading padding tiles that round the count up to the ring size
 };
@@ -278,25 +302,36 @@ __device__ __forceinline__ Frags masked(const Frags& F, bool live) {
     return r;
 }
 
-// Ring slot kt (tile kt - pad), held in stage S = kt % 4. Entering: F0
+// Ring slot kt (tile kt - pad), held in stage S = kt % stages. Entering: F0
 // holds (or is receiving) the slot's first-step fragments, and the copies of
-// slots kt + 1 .. kt + 3 are in flight or done. The first step's MFMAs run
+// the following slots up to kt + stages - 1 are in flight or done. The first step's MFMAs run
 // while the second step's fragments are read. Then: wait for slot kt + 1,
 // barrier (slot kt + 1 is complete for every wave, and stage S has been read
-// by every wave), start the copies of slot kt + 4 into stage S and read slot
+// by every wave), start the copies of slot kt + stages into stage S and read slot
 // kt + 1's first-step fragments while the second step's MFMAs run. After the
 // last slot these extra copies and reads are not used.
+// One k step of stage S with fragments C while the next step's are read
+// into N.
+template <int S, int STEP>
+__device__ __forceinline__ void inner_step(const Ctx& c, bool live, Frags& C, Frags& N, Acc& acc) {
+    load_frags<S>(c.wt, c.wf, c.off[STEP + 1], N);
+    mfma_step(masked(C, live), acc);
+    sched_reads_among_mfma();
+}
+
 template <int S>
 __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
     constexpr int SN = (S + 1) % kFcStages;
     const bool live = kt >= c.pad;
-    load_frags<S>(c.wt, c.wf, c.off1, F1);
-    mfma_step(masked(F0, live), acc);
-    sched_reads_among_mfma();
-    wait_copies_and_lds<2 * kFcCopies>();              // slots kt + 2 and kt + 3 may be pending
+    inner_step<S, 0>(c, live, F0, F1, acc);
+    if constexpr (kFcSteps == 4) {
+        inner_step<S, 1>(c, live, F1, F0, acc);
+        inner_step<S, 2>(c, live, F0, F1, acc);
+    }
+    wait_copies_and_lds<(kFcStages - 2) * kFcCopies>();  // slots kt + 2 .. may be pending
     ring_barrier();
     copy_tile<S>(c.src, source_tile(c, kt + kFcStages));
-    load_frags<SN>(c.wt, c.wf, c.off0, F0);
+    load_frags<SN>(c.wt, c.wf, c.off[0], F0);
     mfma_step(masked(F1, live), acc);
     sched_copies_reads_among_mfma();
 }
@@ -329,26 +364,29 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
         // A fragment lane reads row lane % 32 of a 32-row tile and chunk
         // 2 s + lane / 32 in step s.
         const int frow = lane % 32;
-        c.off0 = frow * kFcRowElems + chunk_slot(frow, lane / 32) * 8;
-        c.off1 = frow * kFcRowElems + chunk_slot(frow, 2 + lane / 32) * 8;
+#pragma unroll
+        for (int st = 0; st < kFcSteps; ++st)
+            c.off[st] = frow * kFcRowElems + chunk_slot(frow, 2 * st + lane / 32) * 8;
     }
 
     // Fill the ring and wait for slot 0.
     copy_tile<0>(c.src, source_tile(c, 0));
     copy_tile<1>(c.src, source_tile(c, 1));
-    copy_tile<2>(c.src, source_tile(c, 2));
-    copy_tile<3>(c.src, source_tile(c, 3));
-    wait_copies_and_lds<3 * kFcCopies>();
+    if constexpr (kFcStages > 2) copy_tile<2 % kFcStages>(c.src, source_tile(c, 2));
+    if constexpr (kFcStages > 3) copy_tile<3 % kFcStages>(c.src, source_tile(c, 3));
+    if constexpr (kFcStages > 4) copy_tile<4 % kFcStages>(c.src, source_tile(c, 4));
+    wait_copies_and_lds<(kFcStages - 1) * kFcCopies>();
     ring_barrier();
     Frags F0, F1;
-    load_frags<0>(c.wt, c.wf, c.off0, F0);
+    load_frags<0>(c.wt, c.wf, c.off[0], F0);
 
     // unrolled over the ring so that every stage is named statically
     for (int kt = 0; kt < slots; kt += kFcStages) {
         k_tile<0>(c, kt, F0, F1, acc);
         k_tile<1>(c, kt + 1, F0, F1, acc);
-        k_tile<2>(c, kt + 2, F0, F1, acc);
-        k_tile<3>(c, kt + 3, F0, F1, acc);
+        if constexpr (kFcStages > 2) k_tile<2 % kFcStages>(c, kt + 2, F0, F1, acc);
+        if constexpr (kFcStages > 3) k_tile<3 % kFcStages>(c, kt + 3, F0, F1, acc);
+        if constexpr (kFcStages > 4) k_tile<4 % kFcStages>(c, kt + 4, F0, F1, acc);
     }
     // No copy may still be writing LDS when the workgroup ends.
     wait_copies_and_lds<0>();
