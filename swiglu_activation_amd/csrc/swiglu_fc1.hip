@@ -319,10 +319,11 @@ __device__ __forceinline__ void inner_step(const Ctx& c, bool live, Frags& C, Fr
     sched_reads_among_mfma();
 }
 
-template <int S>
+// MASK: the slot may be a padding slot (only in the first pass over the ring).
+template <int S, bool MASK>
 __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
     constexpr int SN = (S + 1) % kFcStages;
-    const bool live = kt >= c.pad;
+    const bool live = !MASK || kt >= c.pad;
     inner_step<S, 0>(c, live, F0, F1, acc);
     if constexpr (kFcSteps == 4) {
         inner_step<S, 1>(c, live, F1, F0, acc);
@@ -334,6 +335,16 @@ __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F
     load_frags<SN>(c.wt, c.wf, c.off[0], F0);
     mfma_step(masked(F1, live), acc);
     sched_copies_reads_among_mfma();
+}
+
+// Slots kt .. kt + stages - 1: one pass over the ring.
+template <bool MASK>
+__device__ __forceinline__ void ring_pass(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
+    k_tile<0, MASK>(c, kt, F0, F1, acc);
+    k_tile<1, MASK>(c, kt + 1, F0, F1, acc);
+    if constexpr (kFcStages > 2) k_tile<2 % kFcStages, MASK>(c, kt + 2, F0, F1, acc);
+    if constexpr (kFcStages > 3) k_tile<3 % kFcStages, MASK>(c, kt + 3, F0, F1, acc);
+    if constexpr (kFcStages > 4) k_tile<4 % kFcStages, MASK>(c, kt + 4, F0, F1, acc);
 }
 
 __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint32_t f_tiles,
@@ -381,13 +392,9 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     load_frags<0>(c.wt, c.wf, c.off[0], F0);
 
     // unrolled over the ring so that every stage is named statically
-    for (int kt = 0; kt < slots; kt += kFcStages) {
-        k_tile<0>(c, kt, F0, F1, acc);
-        k_tile<1>(c, kt + 1, F0, F1, acc);
-        if constexpr (kFcStages > 2) k_tile<2 % kFcStages>(c, kt + 2, F0, F1, acc);
-        if constexpr (kFcStages > 3) k_tile<3 % kFcStages>(c, kt + 3, F0, F1, acc);
-        if constexpr (kFcStages > 4) k_tile<4 % kFcStages>(c, kt + 4, F0, F1, acc);
-    }
+    // the padding slots all fall in the first pass, the only one that masks
+    ring_pass<true>(c, 0, F0, F1, acc);
+    for (int kt = kFcStages; kt < slots; kt += kFcStages) ring_pass<false>(c, kt, F0, F1, acc);
     // No copy may still be writing LDS when the workgroup ends.
     wait_copies_and_lds<0>();
 

@@ -111,3 +111,35 @@ def test_fc1_argument_errors():
         sw.swiglu_fc1_fwd(a, torch.zeros(96, 64, dtype=torch.bfloat16, device="cuda"))  # n = 48
     with pytest.raises(ValueError):
         sw.swiglu_fc1_fwd(a, w, a[:, :64])                               # y overlaps a
+
+
+@pytest.mark.parametrize("hidden,n", [(4096, 4096), (8192, 32768)])
+def test_fc1_full_size_sampled(hidden, n):
+    """The benchmark's shapes and launch (8192 tokens, one call writing y,
+    then one also writing the product). Inputs are drawn on the device with
+    a seeded torch generator (N(0,1) activations, N(0,1/hidden) weights,
+    rounded to bf16); y and the product are compared with the oracle on a
+    64 x 64 block of sampled (token, feature) pairs that includes the first
+    and last rows and the edges of the workgroup tiles."""
+    m = 8192
+    print(f"[fc1 full] tokens {m} hidden {hidden} n {n}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(hidden + n)
+    a = torch.randn(m, hidden, device="cuda", generator=gen).bfloat16()
+    w = (torch.randn(2 * n, hidden, device="cuda", generator=gen) / hidden ** 0.5).bfloat16()
+    y = sw.swiglu_fc1_fwd(a, w)
+    y2, x = sw.swiglu_fc1_fwd(a, w, x_out=True)
+    torch.cuda.synchronize()
+    assert gu.bits_equal(y, y2)
+    rng = np.random.default_rng(hidden + n)
+    toks = np.unique(np.concatenate([[0, 1, 255, 256, 511, m - 1],
+                                     rng.choice(m, 58, replace=False)]))
+    feats = np.unique(np.concatenate([[0, 63, 64, 127, 128, n - 1],
+                                      rng.choice(n, 58, replace=False)]))
+    ti = torch.from_numpy(toks).cuda()
+    fi = torch.from_numpy(feats).cuda()
+    a_s = gu.from_dev(a[ti])
+    w_s = gu.from_dev(torch.cat([w[fi], w[fi + n]]))
+    y_s = y[ti][:, fi]
+    x_s = torch.cat([x[ti][:, fi], x[ti][:, fi + n]], dim=1)
+    _check(a_s, w_s, y_s, x_s)
+    del a, w, y, y2, x
