@@ -321,6 +321,91 @@ def test_bf16_ulp_distance():
     assert np.all(np.diff(o[order]) >= 0)
 
 
+def _is_nearest_bf16(v: Fraction, bits: int) -> bool:
+    """bits is a nearest (ties to even) bf16 of the exact value v; a result
+    of zero may carry either sign."""
+    m = bits & 0x7FFF
+    if m == 0:
+        return abs(v) <= Fraction(2) ** -134        # half the smallest subnormal (a tie goes to 0)
+    if v == 0 or (v < 0) != bool(bits & 0x8000):
+        return False
+    a = abs(v)
+    if m == 0x7F80:
+        return a >= Fraction(255) * Fraction(2) ** 120 + Fraction(2) ** 119
+    d = abs(_bf16_frac(m) - a)
+    for nb in (m - 1, m + 1):
+        if 0 <= nb <= 0x7F7F:
+            dn = abs(_bf16_frac(nb) - a)
+            if dn < d or (dn == d and nb % 2 == 0):
+                return False
+    return True
+
+
+def _mp_to_fraction(x) -> Fraction:
+    sign, man, exp, _ = x._mpf_                          # value = (-1)^sign * man * 2^exp
+    return (-1 if sign else 1) * Fraction(int(man)) * Fraction(2) ** int(exp)
+
+
+def test_bf16_rounding_of_oracle_equals_50_digit_rounding_on_every_gate():
+    """For every finite bf16 gate value g, the oracle's float64 silu(g) and
+    silu'(g) (the forward and dgate with u = dy = 1), rounded once to bf16,
+    are the nearest bf16 values of the 50-digit results. The derivative is
+    taken by the quotient rule, 1/(1+e^-g) + g e^-g / (1+e^-g)^2, not in the
+    oracle's form.
+
+    One exception, asserted exactly: for a gate below 2^-125 in magnitude
+    with an odd last bit, silu(g) = g/2 + g^2/4 + ... where float64 keeps
+    only g/2, a bf16 subnormal plus exactly half a step; the oracle rounds
+    that tie to even, the exact value lies just past it. Those forwards
+    differ by one subnormal step (2^-133)."""
+    import mpmath
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    g = oracle.bf16_bits_to_f64(allbits)
+    g = g[np.isfinite(g)]
+    y_bits = oracle.round_f64_to_bf16_bits(oracle.silu(g))
+    d_bits = oracle.round_f64_to_bf16_bits(oracle.silu_grad(g))
+    tiny = mpmath.mpf(2) ** -140
+    bad = []
+    with mpmath.workdps(50):
+        for gv, yb, db in zip(g.tolist(), y_bits.tolist(), d_bits.tolist()):
+            G = mpmath.mpf(gv)
+            e = mpmath.exp(-G)
+            silu = G / (1 + e)
+            grad = 1 / (1 + e) + G * e / (1 + e) ** 2
+            for val, bits in ((silu, yb), (grad, db)):
+                if abs(val) < tiny:
+                    ok = (bits & 0x7FFF) == 0
+                else:
+                    ok = _is_nearest_bf16(_mp_to_fraction(val), int(bits))
+                if not ok:
+                    bad.append((gv, val is silu, int(bits)))
+    tie_cases = 0
+    for gv, is_fwd, bits in bad:
+        # only forwards at gates whose half is subnormal and whose float64 value is an exact tie
+        assert is_fwd and 0 < abs(gv) < 2.0 ** -125, (gv, is_fwd, hex(bits))
+        y64 = float(oracle.silu(np.array([gv]))[0])
+        assert y64 == gv / 2
+        scaled = abs(y64) * 2.0 ** 133                  # in units of the smallest subnormal
+        assert scaled % 1 == 0.5, (gv, scaled)
+        tie_cases += 1
+    odd_tiny = int(np.sum((np.abs(g) < 2.0 ** -125) & (g != 0) &
+                          (oracle.round_f64_to_bf16_bits(np.abs(g)) % 2 == 1)))
+    assert tie_cases <= odd_tiny == 256
+    print(f"{tie_cases} tie cases of {g.size} gates")
+
+
+def test_minimiser_identities():
+    """At g0: sigma(g0) = 1 + 1/g0 (silu'(g0) = 0 solved for sigma), and the
+    bracket h(g) = silu'(g) / sigma(g) = 1 + g (1 - sigma(g)) crosses zero
+    with slope exactly 1 (h' = (1 - sigma)(1 - g sigma) = (-1/g0)(-g0))."""
+    g0 = oracle.G0
+    assert abs(oracle.sigmoid(np.array([g0]))[0] - (1 + 1 / g0)) < 1e-15
+    d = 1e-6
+    gs = np.array([g0 - d, g0 + d])
+    h = oracle.silu_grad(gs) / oracle.sigmoid(gs)
+    assert abs((h[1] - h[0]) / (2 * d) - 1.0) < 1e-8
+
+
 # --------------------------------------------------------------------------
 # Golden fixture (written by tests/golden/make_golden.py from the oracle)
 # --------------------------------------------------------------------------
