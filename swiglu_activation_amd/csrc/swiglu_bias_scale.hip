@@ -25,6 +25,9 @@ using namespace swiglu_impl;
 #ifndef SWIGLU_BS_ROWS_PER_GROUP
 #define SWIGLU_BS_ROWS_PER_GROUP 128   // rows reduced in registers per block (backward)
 #endif
+#ifndef SWIGLU_BS_PREFETCH
+#define SWIGLU_BS_PREFETCH 1           // load the next row while computing this one (backward)
+#endif
 #ifndef SWIGLU_BS_INTERLEAVE
 #define SWIGLU_BS_INTERLEAVE 1         // group y takes rows y, y+G, y+2G, ... (else a band)
 #endif
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
 // Partial sums of a backward over rows [row0 + y*R, row0 + (y+1)*R) for the
 // column tile x. Writes dz for every element; part_db[group][k] gets this
 // group's column sums (k in [0, 2n): gate columns, then up columns) and
-// part_ds[row][x][w] wave w's share of each row's ds. Fixed summation order
+// part_ds[x][w][row] wave w's share of each row's ds. Fixed summation order
 // throughout: each lane adds its rows in order, each wave's share is a fixed
 // butterfly, and the second pass adds tiles and waves in order.
 struct BsGeom {
@@ -81,6 +84,7 @@ struct BsGeom {
     int64_t n;          // half width (elements)
     int64_t group0;     // global index of this launch's first row group
     int64_t row0;       // global index of this launch's first row
+    int64_t total_rows; // rows of the whole problem (the stride of part_ds)
     uint32_t nv;        // vectors per half row
     uint32_t tiles;     // column tiles per row (= gridDim.x)
 };
@@ -103,6 +107,26 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
     v += dpp_f<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Widens VEC elements of T held as raw bits (as Vec<T, VEC>::load does
+// after its load).
+template <typename T, int VEC>
+__device__ __forceinline__ void widen_bits(typename Vec<T, VEC>::R r, float (&f)[VEC]) {
+    constexpr int kBytes = Vec<T, VEC>::kBytes;
+    if constexpr (sizeof(T) == 4) {
+        __builtin_memcpy(f, &r, sizeof(r));
+    } else if constexpr (kBytes == 2) {
+        f[0] = __uint_as_float((uint32_t)r << 16);
+    } else {
+        uint32_t w[kBytes / 4];
+        __builtin_memcpy(w, &r, sizeof(r));
+#pragma unroll
+        for (int i = 0; i < kBytes / 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);           // lower address: low half
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
 }
 
 template <typename T, int VEC, bool IN_PLACE>
@@ -140,16 +164,12 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs_kernel(
         Vec<T, VEC>::template load<true>(bu + c, buv);
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int j = 0; j < kBsRows; ++j) {
-        const int64_t row = r_first + j * r_step;
-        if (row >= G.rows) break;                     // uniform
-        const float s = sc != nullptr ? sc[row * scs] : 1.0f;
+    // The row's math and stores; p collects dy * silu(z_g) * z_u for dscale.
+    auto row_step = [&](int64_t row, float s, const float (&g)[VEC], const float (&u)[VEC],
+                        const float (&d)[VEC]) {
         float p = 0.0f;
         if (active) {
-            float g[VEC], u[VEC], d[VEC], dg[VEC], du[VEC];
-            Vec<T, VEC>::load(gp + row * gs + c, g);
-            Vec<T, VEC>::load(up + row * us + c, u);
-            Vec<T, VEC>::load(dyp + row * dys + c, d);
+            float dg[VEC], du[VEC];
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
                 float zg, zlo;
@@ -173,9 +193,62 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs_kernel(
             // One partial per (row, tile, wave); the second pass adds the
             // tiles and waves of a row in order.
             const float w = wave_sum(p);
-            if (lane == 0) part_ds[((G.row0 + row) * G.tiles + blockIdx.x) * kWaves + wave] = w;
+            if (lane == 0)
+                part_ds[((int64_t)blockIdx.x * kWaves + wave) * G.total_rows + G.row0 + row] = w;
         }
+    };
+#if SWIGLU_BS_PREFETCH
+    // Row j + 1 is loaded (as raw bits) while row j is computed, so two rows
+    // of loads are in flight per wave.
+    typedef typename Vec<T, VEC>::R R;
+    R gr{}, ur{}, dr{};
+    auto load_row = [&](int64_t row, R& gg, R& uu, R& dd) {
+        if (active) {
+            gg = load_raw<R>(gp + row * gs + c);
+            uu = load_raw<R>(up + row * us + c);
+            dd = load_raw<R>(dyp + row * dys + c);
+        }
+    };
+    float s = 1.0f;                                   // the row's scale, also one row ahead
+    if (r_first < G.rows) {
+        load_row(r_first, gr, ur, dr);
+        if (sc != nullptr) s = sc[r_first * scs];
     }
+    for (int j = 0; j < kBsRows; ++j) {
+        const int64_t row = r_first + j * r_step;
+        if (row >= G.rows) break;                     // uniform
+        const int64_t nrow = row + r_step;
+        R gn{}, un{}, dn{};
+        float sn = 1.0f;
+        const bool more = j + 1 < kBsRows && nrow < G.rows;   // uniform
+        if (more) {
+            load_row(nrow, gn, un, dn);
+            if (sc != nullptr) sn = sc[nrow * scs];
+        }
+        float g[VEC], u[VEC], d[VEC];
+        widen_bits<T, VEC>(gr, g);
+        widen_bits<T, VEC>(ur, u);
+        widen_bits<T, VEC>(dr, d);
+        row_step(row, s, g, u, d);
+        gr = gn;
+        ur = un;
+        dr = dn;
+        s = sn;
+    }
+#else
+    for (int j = 0; j < kBsRows; ++j) {
+        const int64_t row = r_first + j * r_step;
+        if (row >= G.rows) break;                     // uniform
+        const float s = sc != nullptr ? sc[row * scs] : 1.0f;
+        float g[VEC], u[VEC], d[VEC];
+        if (active) {
+            Vec<T, VEC>::load(gp + row * gs + c, g);
+            Vec<T, VEC>::load(up + row * us + c, u);
+            Vec<T, VEC>::load(dyp + row * dys + c, d);
+        }
+        row_step(row, s, g, u, d);
+    }
+#endif
     if (part_db != nullptr && active) {
         float* pg = part_db + (G.group0 + blockIdx.y) * (2 * G.n) + c;
 #pragma unroll
@@ -195,7 +268,16 @@ __global__ __launch_bounds__(kBlock) void swiglu_sum_partials_kernel(
     if (k >= width) return;
     const float* p = part + k * kstride;
     float acc = 0.0f;
-    for (int64_t j = 0; j < count; ++j) acc += p[j * jstride];
+    int64_t j = 0;
+    // eight loads in flight, added in the same order as the plain loop
+    for (; j + 8 <= count; j += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = p[(j + i) * jstride];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += v[i];
+    }
+    for (; j < count; ++j) acc += p[j * jstride];
     out[k * out_stride] = acc;
 }
 
@@ -248,7 +330,7 @@ swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
 }
 
 // Workspace layout of the backward: [part_db: groups x 2n fp32]
-// [part_ds: rows x tiles x waves fp32],
+// [part_ds: tiles x waves x rows fp32],
 // each part starting on a 256-byte boundary. tiles is bounded by the
 // single-element access width, so the size does not depend on alignment.
 int64_t bs_groups(int64_t rows) { return (rows + kBsRows - 1) / kBsRows; }
@@ -311,6 +393,7 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
     G.n = n;
     G.nv = nv;
     G.tiles = tiles;
+    G.total_rows = rows;
     void* args[] = {&dyp, &dys, &gp, &gs, &upp, &us, &dgp, &dgs, &dup, &dus,
                     &bg, &bu, &sc, &scs, &part_db, &part_ds, &G};
     const int64_t rows_per_launch = (int64_t)kMaxGridY * kBsRows;
@@ -333,8 +416,8 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
     if (dbias != nullptr)
         st = sum_partials(part_db, groups, 2 * n, 1, 2 * n, dbias, 1, stream);
     if (st == SWIGLU_OK && dscale != nullptr)
-        st = sum_partials(part_ds, (int64_t)tiles * kWaves, 1, (int64_t)tiles * kWaves, rows,
-                          dscale, dscale_stride, stream);
+        st = sum_partials(part_ds, (int64_t)tiles * kWaves, rows, 1, rows, dscale, dscale_stride,
+                          stream);
     return st;
 }
 
