@@ -138,6 +138,40 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
     return out
 
 
+def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
+    """Bias + per-token scale variants on the workload's tensors: forward,
+    and backward with dx, dbias and dscale (the reductions included)."""
+    import numpy as np
+    import torch
+
+    import swiglu_activation_amd as sw
+    tdt = x.dtype
+    e = w.elem_bytes
+    fwd_bytes, bwd_bytes = 3 * e * w.rows * w.n, 5 * e * w.rows * w.n
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    bias_t = (torch.randn(2 * w.n, device=dev, generator=gen) * 0.5).to(tdt)
+    scale_t = torch.rand(w.shape[:-1], device=dev, generator=gen) * 0.95 + 0.05
+    ws = torch.empty(sw.swiglu_gateup_bias_scale_workspace_size(w.rows, w.n, True, True),
+                     dtype=torch.uint8, device=dev)
+    bt = []
+    for k in range(iters + 2):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        sw.swiglu_gateup_bias_scale_fwd(x, bias_t, scale_t, y)
+        b.record(stream)
+        sw.swiglu_gateup_bias_scale_bwd(dy, x, bias_t, scale_t, dx, workspace=ws)
+        c.record(stream)
+        c.synchronize()
+        if k >= 2:
+            bt.append((a.elapsed_time(b), b.elapsed_time(c)))
+    bf, bb = float(np.mean([t[0] for t in bt])), float(np.mean([t[1] for t in bt]))
+    return {"fwd_ms": round(bf, 5), "bwd_ms": round(bb, 5),
+            "fwd_GBps": round(fwd_bytes / bf / 1e6, 1),
+            "bwd_GBps": round(bwd_bytes / bb / 1e6, 1),
+            "what": "z = x + bias, y = s * silu(z_g) * z_u; bwd writes dx, dbias, "
+                    "dscale (GB/s on the base op's bytes)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +186,9 @@ def main():
     ap.add_argument("--fc1-only", action="store_true",
                     help="time only the fc1 projection with the SwiGLU epilogue, print its "
                          "figures as one JSON line, and exit (for profiling runs)")
+    ap.add_argument("--bias-scale-only", action="store_true",
+                    help="time only the bias / per-token-scale forward and backward on the "
+                         "workload, print their figures as one JSON line, and exit")
     ap.add_argument("--calib", action="store_true",
                     help="also run plain 1 GiB copies (torch copy_ and an elementwise "
                          "negation) as the byte-counter calibration for rocprofv3 --pmc")
@@ -198,6 +235,10 @@ def main():
     y = torch.empty(w.shape[:-1] + (w.n,), dtype=tdt, device=dev)
     dx = torch.empty(w.shape, dtype=tdt, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.bias_scale_only:
+        res = bias_scale_leg(dev, stream, w, x, dy, y, dx, iters=args.steps)
+        print(json.dumps({"bias_scale": res}), flush=True)
+        return
 
     e = w.elem_bytes
     pairs = w.rows * w.n
@@ -320,32 +361,9 @@ def main():
                                       "fwd_GBps": round(fwd_bytes / tf / 1e6, 1),
                                       "bwd_GBps": round(bwd_bytes / tb / 1e6, 1)}
         log(f"[bench] autograd step {ag_ms:.4f} ms; two-tensor fwd {tf:.4f} ms bwd {tb:.4f} ms")
-        # Bias + per-token scale variants on the same tensors: forward, and
-        # backward with dx, dbias and dscale (the reductions included).
-        gen = torch.Generator(device=dev).manual_seed(w.seed)
-        bias_t = (torch.randn(2 * w.n, device=dev, generator=gen) * 0.5).to(tdt)
-        scale_t = torch.rand(w.shape[:-1], device=dev, generator=gen) * 0.95 + 0.05
-        ws = torch.empty(sw.swiglu_gateup_bias_scale_workspace_size(w.rows, w.n, True, True),
-                         dtype=torch.uint8, device=dev)
-        bt = []
-        for k in range(12):
-            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            a.record(stream)
-            sw.swiglu_gateup_bias_scale_fwd(x, bias_t, scale_t, y)
-            b.record(stream)
-            sw.swiglu_gateup_bias_scale_bwd(dy, x, bias_t, scale_t, dx, workspace=ws)
-            c.record(stream)
-            c.synchronize()
-            if k >= 2:
-                bt.append((a.elapsed_time(b), b.elapsed_time(c)))
-        bf, bb = float(np.mean([t[0] for t in bt])), float(np.mean([t[1] for t in bt]))
-        passes["bias_scale"] = {"fwd_ms": round(bf, 5), "bwd_ms": round(bb, 5),
-                                "fwd_GBps": round(fwd_bytes / bf / 1e6, 1),
-                                "bwd_GBps": round(bwd_bytes / bb / 1e6, 1),
-                                "what": "z = x + bias, y = s * silu(z_g) * z_u; bwd writes dx, dbias, "
-                                        "dscale (GB/s on the base op's bytes)"}
-        log(f"[bench] bias+scale fwd {bf:.4f} ms, bwd {bb:.4f} ms")
-        del ws
+        passes["bias_scale"] = bias_scale_leg(dev, stream, w, x, dy, y, dx)
+        log(f"[bench] bias+scale fwd {passes['bias_scale']['fwd_ms']:.4f} ms, "
+            f"bwd {passes['bias_scale']['bwd_ms']:.4f} ms")
         passes["fc1_swiglu"] = fc1_leg(dev, stream, w.rows)
         if (w.n * e) % 16 == 0 and w.rows <= 65535:
             # The same access patterns with no arithmetic: the best this memory

@@ -143,3 +143,24 @@ def test_fc1_full_size_sampled(hidden, n):
     x_s = torch.cat([x[ti][:, fi], x[ti][:, fi + n]], dim=1)
     _check(a_s, w_s, y_s, x_s)
     del a, w, y, y2, x
+
+
+def test_fc1_strided_operands():
+    """a and w as column slices of wider buffers (row strides k + 64 and
+    k + 128), the product written into a wider buffer whose extra columns
+    must stay untouched."""
+    m, n, k = 384, 256, 512
+    print(f"[fc1 strided] m={m} n={n} k={k}", flush=True)
+    a_h, w_h = _case(m, n, k, seed=9)
+    ab = torch.zeros(m, k + 64, dtype=torch.bfloat16, device="cuda")
+    ab[:, :k] = gu.to_dev(a_h, "bf16")
+    wb = torch.zeros(2 * n, k + 128, dtype=torch.bfloat16, device="cuda")
+    wb[:, :k] = gu.to_dev(w_h, "bf16")
+    xb = torch.full((m, 2 * n + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y, x = sw.swiglu_fc1_fwd(ab[:, :k], wb[:, :k], x_out=xb[:, :2 * n])
+    torch.cuda.synchronize()
+    assert torch.isnan(xb[:, 2 * n:]).all()
+    _check(a_h, w_h, y, x)
+    y_dense = sw.swiglu_fc1_fwd(gu.to_dev(a_h, "bf16"), gu.to_dev(w_h, "bf16"))
+    torch.cuda.synchronize()
+    assert gu.bits_equal(y, y_dense)
