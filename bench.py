@@ -172,6 +172,77 @@ def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
                     "dscale (GB/s on the base op's bytes)"}
 
 
+def configs_leg(dev, stream, skip: str, replays: int = 10):
+    """Every other workload's forward and backward (in place where the
+    workload says so), as context for the headline: device-drawn inputs of
+    the workload's shape and dtype (timing does not depend on the values),
+    rotated over enough buffer sets that each launch reads data last touched
+    more than 512 MB earlier, so the 256 MB Infinity Cache cannot serve it.
+    The launches over all sets are captured in one HIP graph per pass and the
+    graph is replayed, so host launch overhead does not show in the times of
+    the short kernels (these workloads run 3 to 140 us per launch)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import swiglu_activation_amd as sw
+    out = {}
+    for w in synth.WORKLOADS.values():
+        if w.name == skip:
+            continue
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        e = w.elem_bytes
+        fwd_bytes, bwd_bytes = 3 * e * w.rows * w.n, 5 * e * w.rows * w.n
+        # (at most 64 sets: the tiny workload is bound by launch latency anyway)
+        sets = min(64, max(2, -(-(512 << 20) // fwd_bytes) + 1))
+        gen = torch.Generator(device=dev).manual_seed(w.seed)
+        bufs = []
+        for _ in range(sets):
+            x = torch.randn(w.shape, device=dev, generator=gen).to(tdt)
+            dy = torch.randn(w.shape[:-1] + (w.n,), device=dev, generator=gen).to(tdt)
+            y = torch.empty(w.shape[:-1] + (w.n,), dtype=tdt, device=dev)
+            dx = None if w.in_place else torch.empty_like(x)
+            bufs.append((x, dy, y, dx))
+
+        def fwd_pass():
+            for x, dy, y, dx in bufs:
+                sw.swiglu_gateup_fwd(x, y)
+
+        def bwd_pass():
+            for x, dy, y, dx in bufs:
+                if w.in_place:
+                    sw.swiglu_gateup_bwd(dy, x, in_place=True)
+                else:
+                    sw.swiglu_gateup_bwd(dy, x, dx)
+
+        res = {}
+        for name, fn, nbytes in (("fwd", fwd_pass, fwd_bytes), ("bwd", bwd_pass, bwd_bytes)):
+            fn()                                              # warm up outside the graph
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            g.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(replays):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                b.synchronize()
+                ts.append(a.elapsed_time(b) / sets)
+            t = float(np.median(ts))
+            res[f"{name}_us"] = round(t * 1e3, 2)
+            res[f"{name}_GBps"] = round(nbytes / t / 1e6, 1)
+            del g
+        res.update({"bwd": "in place" if w.in_place else "out of place", "buffer_sets": sets,
+                    "timing": "HIP graph of one launch per buffer set, replayed"})
+        out[w.name] = res
+        del bufs
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -364,6 +435,10 @@ def main():
         passes["bias_scale"] = bias_scale_leg(dev, stream, w, x, dy, y, dx)
         log(f"[bench] bias+scale fwd {passes['bias_scale']['fwd_ms']:.4f} ms, "
             f"bwd {passes['bias_scale']['bwd_ms']:.4f} ms")
+        passes["other_workloads"] = configs_leg(dev, stream, w.name)
+        log("[bench] other workloads: " + ", ".join(
+            f"{k} fwd {v['fwd_GBps']:.0f} bwd {v['bwd_GBps']:.0f} GB/s"
+            for k, v in passes["other_workloads"].items()))
         passes["fc1_swiglu"] = fc1_leg(dev, stream, w.rows)
         if (w.n * e) % 16 == 0 and w.rows <= 65535:
             # The same access patterns with no arithmetic: the best this memory
