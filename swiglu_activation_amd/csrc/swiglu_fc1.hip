@@ -53,6 +53,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_XCD
 #define SWIGLU_FC_XCD 0         // give each XCD a contiguous range of the launch order
 #endif
+#ifndef SWIGLU_FC_CPOL
+#define SWIGLU_FC_CPOL 0        // cache-policy bits of the copies (gfx950: 1 sc0, 2 nt)
+#endif
 #ifndef SWIGLU_FC_SCHED
 #define SWIGLU_FC_SCHED 1       // pin the interleaving of MFMAs and memory instructions
 #endif
@@ -164,7 +167,7 @@ __device__ __forceinline__ void copy_tile(const Sources& src, int t) {
         uint16_t* dst = stage<S>() + (i * kFcWaves + wave) * kFcCopyRows * kFcRowElems;
         __builtin_amdgcn_global_load_lds(
             static_cast<const void*>(src.p[i] + (int64_t)t * kFcTileK),
-            (lds_void*)(dst), 16, 0, 0);
+            (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
     }
 }
 
