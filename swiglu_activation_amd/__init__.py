@@ -449,12 +449,16 @@ def swiglu_fc1_fwd(a, w, y=None, *, x_out=None, stream=None):
     _, ldw = _rows_and_stride(w, "w")
     if y is None:
         y = torch.empty(tuple(a.shape[:-1]) + (n,), dtype=a.dtype, device=a.device)
+    if y.dtype != torch.bfloat16:
+        raise ValueError("y must be bfloat16")
     ldy = _same_rows(y, m, n, "y")
     want_x = x_out is not None and x_out is not False
     if x_out is True:
         x_out = torch.empty(tuple(a.shape[:-1]) + (2 * n,), dtype=a.dtype, device=a.device)
     xp, ldx = None, 0
     if want_x:
+        if x_out.dtype != torch.bfloat16:
+            raise ValueError("x_out must be bfloat16")
         ldx = _same_rows(x_out, m, 2 * n, "x_out")
         xp = x_out.data_ptr()
     with torch.cuda.device(a.device):

@@ -136,6 +136,13 @@ def test_binding_rejects_host_tensors():
         sw.swiglu_gateup_fwd(x)
     with pytest.raises(ValueError):
         sw.swiglu_gateup_bwd(torch.zeros(4, 8), x)
+    with pytest.raises(ValueError):
+        sw.swiglu_gateup_bias_scale_fwd(x, torch.zeros(16))
+    with pytest.raises(ValueError):
+        sw.swiglu_silu_mul_fwd(torch.zeros(4, 8), torch.zeros(4, 8))
+    with pytest.raises(ValueError):
+        sw.swiglu_fc1_fwd(torch.zeros(4, 64, dtype=torch.bfloat16),
+                          torch.zeros(128, 64, dtype=torch.bfloat16))
 
 
 def test_row_flattening():

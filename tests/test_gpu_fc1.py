@@ -111,6 +111,10 @@ def test_fc1_argument_errors():
         sw.swiglu_fc1_fwd(a, torch.zeros(96, 64, dtype=torch.bfloat16, device="cuda"))  # n = 48
     with pytest.raises(ValueError):
         sw.swiglu_fc1_fwd(a, w, a[:, :64])                               # y overlaps a
+    with pytest.raises(ValueError):
+        sw.swiglu_fc1_fwd(a, w, torch.empty(8, 64, device="cuda"))      # float32 y
+    with pytest.raises(ValueError):
+        sw.swiglu_fc1_fwd(a, w, x_out=torch.empty(8, 128, device="cuda"))  # float32 x_out
 
 
 @pytest.mark.parametrize("hidden,n", [(4096, 4096), (8192, 32768)])
