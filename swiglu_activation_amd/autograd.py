@@ -21,19 +21,28 @@ Behaviour follows the Liger-Kernel Megatron SwiGLU page:
 * §Background: the two-tensor op for models whose gate and up projections
   are separate tensors.
 
-Every computation runs in libswiglu_gateup.so; this module only wires it
-into autograd.
+The fc1 projection with the SwiGLU epilogue (Liger-Kernel test/cute page,
+§MLP1 numerical reference: fused MLP1-with-activation variants) is wired in
+as Fc1SwiGLU: the forward is the fused kernel, which also writes the
+[tokens, 2n] product for the backward; the backward is the SwiGLU backward
+kernel followed by the two weight and input GEMMs of the projection (plain
+library GEMMs through torch.matmul).
+
+Every SwiGLU computation runs in libswiglu_gateup.so; this module only wires
+it into autograd.
 """
 
 from __future__ import annotations
 
 import torch
 
-from . import (swiglu_gateup_bias_scale_bwd, swiglu_gateup_bias_scale_fwd, swiglu_gateup_bwd,
-               swiglu_gateup_fwd, swiglu_silu_mul_bwd, swiglu_silu_mul_fwd, _rows_and_stride)
+from . import (swiglu_fc1_fwd, swiglu_gateup_bias_scale_bwd, swiglu_gateup_bias_scale_fwd,
+               swiglu_gateup_bwd, swiglu_gateup_fwd, swiglu_silu_mul_bwd, swiglu_silu_mul_fwd,
+               _rows_and_stride)
 
 __all__ = ["FusedGateUpSiLUMul", "FusedGateUpSiLUMulBiasScale", "SiLUMul", "MegatronSwiGLU",
-           "fused_gate_up_swiglu", "silu_mul", "weighted_swiglu"]
+           "Fc1SwiGLU", "FusedFc1SwiGLU", "fc1_swiglu", "fused_gate_up_swiglu", "silu_mul",
+           "weighted_swiglu"]
 
 
 def _as_row_view(t: torch.Tensor) -> torch.Tensor:
@@ -185,3 +194,48 @@ class MegatronSwiGLU(torch.nn.Module):
         if bias is not None:
             return FusedGateUpSiLUMulBiasScale.apply(intermediate, bias, None, self.in_place)
         return FusedGateUpSiLUMul.apply(intermediate, self.in_place)
+
+
+class Fc1SwiGLU(torch.autograd.Function):
+    """y = silu(a W_g^T) * (a W_u^T) for bf16 a [..., k] and W = [W_g; W_u]
+    [2n, k]. Saves a, W and the product a W^T (written by the fused kernel)."""
+
+    @staticmethod
+    def forward(ctx, a: torch.Tensor, w: torch.Tensor):
+        k = w.shape[1]
+        a2 = _as_row_view(a.reshape(-1, k))
+        y, x = swiglu_fc1_fwd(a2, w, x_out=True)
+        ctx.save_for_backward(a2, w, x)
+        ctx.a_shape = tuple(a.shape)
+        return y.reshape(tuple(a.shape[:-1]) + (w.shape[0] // 2,))
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        a2, w, x = ctx.saved_tensors
+        n = w.shape[0] // 2
+        dy2 = _as_row_view(dy.reshape(-1, n))
+        dx = swiglu_gateup_bwd(dy2, x)                 # [m, 2n] = [dgate | dup]
+        da = dx @ w if ctx.needs_input_grad[0] else None
+        dw = dx.t() @ a2 if ctx.needs_input_grad[1] else None
+        return (da.reshape(ctx.a_shape) if da is not None else None), dw
+
+
+def fc1_swiglu(a: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    return Fc1SwiGLU.apply(a, w)
+
+
+class FusedFc1SwiGLU(torch.nn.Module):
+    """The first half of a SwiGLU MLP: a bias-free fc1 projection to [gate | up]
+    (weight [2 * ffn_hidden, hidden], the Linear layout) with the SwiGLU fused
+    into its epilogue. bf16 only."""
+
+    def __init__(self, hidden: int, ffn_hidden: int, device=None, dtype=torch.bfloat16):
+        super().__init__()
+        if dtype != torch.bfloat16:
+            raise ValueError("FusedFc1SwiGLU is bf16 only")
+        self.weight = torch.nn.Parameter(torch.empty(2 * ffn_hidden, hidden, device=device,
+                                                     dtype=dtype))
+        torch.nn.init.normal_(self.weight, std=hidden ** -0.5)
+
+    def forward(self, a: torch.Tensor) -> torch.Tensor:
+        return Fc1SwiGLU.apply(a, self.weight)

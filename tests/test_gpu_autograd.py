@@ -170,3 +170,38 @@ def test_two_tensor_autograd_and_errors():
         sw.swiglu_silu_mul_bwd(dy, x[:, :512], x[:, 256:768], in_place=True)  # written inputs overlap
     with pytest.raises(ValueError):
         sw.swiglu_silu_mul_bwd(dy, gate.detach(), up.detach(), dgate=dy)   # dgate overlaps dy
+
+
+def test_fc1_swiglu_autograd_matches_float64_reference():
+    """Fc1SwiGLU (fused fc1 + SwiGLU forward, SwiGLU backward kernel and two
+    GEMMs in the backward) against float64 CPU autograd of the same bf16
+    inputs. The GPU chain rounds three times to bf16 on the way (the product,
+    [dgate | dup], and the GEMM outputs), each 2^-9 relative; the bar is 1e-2
+    of the reference's norm, per output."""
+    from swiglu_activation_amd.autograd import FusedFc1SwiGLU, fc1_swiglu
+    rng = np.random.default_rng(70)
+    T, h, f = 2 * 96, 256, 192
+    a_h = oracle.round_f64_to_bf16_bits(rng.standard_normal((T, h)))
+    w_h = oracle.round_f64_to_bf16_bits(rng.standard_normal((2 * f, h)) / np.sqrt(h))
+    g_h = oracle.round_f64_to_bf16_bits(rng.standard_normal((T, f)))
+    a64 = torch.from_numpy(oracle.widen(a_h, "bf16")).requires_grad_(True)
+    w64 = torch.from_numpy(oracle.widen(w_h, "bf16")).requires_grad_(True)
+    z = a64 @ w64.t()
+    y64 = torch.nn.functional.silu(z[:, :f]) * z[:, f:]
+    (y64 * torch.from_numpy(oracle.widen(g_h, "bf16"))).sum().backward()
+    a = gu.to_dev(a_h, "bf16").reshape(2, 96, h).requires_grad_(True)
+    w = gu.to_dev(w_h, "bf16").requires_grad_(True)
+    y = fc1_swiglu(a, w)
+    assert y.shape == (2, 96, f)
+    y.backward(gu.to_dev(g_h, "bf16").reshape(2, 96, f))
+    torch.cuda.synchronize()
+    for got, ref, what in ((y.detach().reshape(T, f), y64.detach(), "y"),
+                           (a.grad.reshape(T, h), a64.grad, "da"), (w.grad, w64.grad, "dw")):
+        err = (got.double().cpu() - ref).norm() / ref.norm()
+        print(f"    {what}: normwise relative error {err.item():.3g}", flush=True)
+        assert err < 1e-2, (what, err.item())
+    m = FusedFc1SwiGLU(h, f, device="cuda")
+    out = m(a.detach())
+    out.float().sum().backward()
+    torch.cuda.synchronize()
+    assert out.shape == (2, 96, f) and m.weight.grad.shape == (2 * f, h)
