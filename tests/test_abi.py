@@ -285,3 +285,27 @@ def test_fc1_empty_problems_launch_nothing(lib):
     assert fc1(lib, None, 64, None, 64, None, 128, None, 0, 0, 128, 64) == sw.SWIGLU_OK
     assert fc1(lib, None, 64, None, 64, None, 0, None, 0, 5, 0, 64) == sw.SWIGLU_OK
     assert fc1(lib, None, 0, None, 0, None, 128, None, 0, 0, 128, 0) == sw.SWIGLU_OK
+
+
+@no_gpu_only
+def test_launch_failure_is_reported():
+    """Arguments that pass every check, on a host with no GPU: the launch
+    itself fails and each entry point returns SWIGLU_ERR_HIP (the status a
+    caller sees for any HIP launch error)."""
+    D = 0x2100000
+    H = sw.SWIGLU_ERR_HIP
+    assert fwd(lib_(), A, 16, B, 8, 4, 8) == H
+    assert bwd(lib_(), A, 8, B, 16, C, 16, 4, 8) == H
+    assert bwd(lib_(), A, 8, B, 16, None, 0, 4, 8, ip=1) == H
+    L = lib_()
+    assert L.swiglu_silu_mul_fwd(A, 8, A + 4096, 8, B, 8, 4, 8, BF16, None) == H
+    assert L.swiglu_silu_mul_bwd(A, 8, B, 8, B + 4096, 8, C, 8, C + 4096, 8, 4, 8, BF16, 0,
+                                 None) == H
+    assert bsf(L, A, 16, B, None, 1, C, 8, 4, 8) == H
+    bias = D + (1 << 16)
+    assert bsb(L, A, 8, B, 16, bias, None, 1, C, 16, D, None, 1, D + 8192, 1 << 20, 4, 8) == H
+    assert fc1(L, A, 64, B, 64, C, 128, None, 0, 4, 128, 64) == H
+
+
+def lib_():
+    return sw.load_library()
