@@ -109,15 +109,17 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
         xbuf = torch.empty(tokens, 2 * n, dtype=torch.bfloat16, device=dev)
         flops = 2.0 * tokens * hidden * 2 * n
 
-        def timed(fn):
+        def timed(fn, warmup=5):
+            # (a longer warm-up than the streaming legs: the first launches of
+            # a matrix-core kernel run while the clocks are still ramping)
             ts = []
-            for k in range(iters + 2):
+            for k in range(iters + warmup):
                 s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s0.record(stream)
                 fn()
                 s1.record(stream)
                 s1.synchronize()
-                if k >= 2:
+                if k >= warmup:
                     ts.append(s0.elapsed_time(s1))
             return float(np.mean(ts))
 
