@@ -86,7 +86,46 @@ def cpu_baseline(w, x_h, dy_h, seconds: float):
     return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"rows 0..{rows} of {w.rows} ({rows * w.n} gate/up pairs) of {w.name}: "
-                      "widen to float64, forward, backward (numpy, one thread)"}
+                      "widen to float64, forward, backward (numpy, one thread)",
+            "other_rows": cpu_baseline_other_rows(w, x_h, dy_h)}
+
+
+def cpu_baseline_other_rows(w, x_h, dy_h, rows: int = 512):
+    """The oracle of the bias / per-token-scale variants and of the fc1
+    projection with the SwiGLU epilogue, each on a small bounded sample and
+    one thread (float64 matmuls limited to one BLAS thread), as the CPU
+    figure beside those rows' GPU legs."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    out = {}
+    rng = np.random.default_rng(w.seed)
+    with threadpool_limits(limits=1):
+        # bias + scale: forward and backward (dx, dbias, dscale) on `rows` rows
+        xf = oracle.widen(x_h[:rows], w.dtype)
+        dyf = oracle.widen(dy_h[:rows], w.dtype)
+        bias = rng.standard_normal(2 * w.n) * 0.5
+        scale = rng.uniform(0.05, 1.0, rows)
+        t0 = time.perf_counter()
+        oracle.oracle_fwd_bias_scale(xf, bias, scale)
+        oracle.oracle_bwd_bias_scale(xf, dyf, bias, scale)
+        dt = time.perf_counter() - t0
+        out["bias_scale"] = {"value": round(8 * w.elem_bytes * rows * w.n / dt / 1e9, 4),
+                             "unit": "GB/s (base op's bytes)", "cores": 1, "seconds": round(dt, 3),
+                             "sample": f"rows 0..{rows} of {w.name} with a bias and a scale"}
+        # fc1 + SwiGLU: 64 tokens against the full weights of hidden 4096, n 4096
+        m, k, n = 64, 4096, 4096
+        a = rng.standard_normal((m, k))
+        wt = rng.standard_normal((2 * n, k)) / np.sqrt(k)
+        t0 = time.perf_counter()
+        y = oracle.oracle_fc1_swiglu(a, wt)
+        dt = time.perf_counter() - t0
+        assert y.shape == (m, n)
+        out["fc1_swiglu"] = {"value": round(2.0 * m * k * 2 * n / dt / 1e12, 6),
+                             "unit": "TFLOP/s", "cores": 1, "seconds": round(dt, 3),
+                             "sample": f"{m} tokens x hidden {k} x n {n} (float64)"}
+    return out
 
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
