@@ -70,20 +70,31 @@ inline int vec_bytes(int esz, const Operand* ops, int nops) {
 // Launch plan. WIDE (n/VEC >= block): block (x, y) owns vectors
 // [x*block, (x+1)*block) of row y. Narrow: block y owns rpb = block / nv
 // whole rows. Rows are covered by launches of at most max_grid_y row groups.
+// Launch plan. Wide rows (at least `block` vectors per half row): a 2D grid
+// of (column tile, row) blocks. Narrow rows: a flat 1D grid over the linear
+// (row, vector) index space, so no lane idles except in the last block; one
+// launch covers at most 2^31 lanes.
 struct Plan {
     bool wide;
-    uint32_t nv, rpb, tiles;     // tiles: column tiles per row (WIDE) or 1
+    uint32_t nv;                 // vectors per half row
+    uint32_t tiles;              // wide: column tiles per row; narrow: 0
     int64_t rows_per_launch;
 };
+
+constexpr int64_t kFlatLanes = (int64_t)1 << 31;   // lanes per narrow launch, at most
 
 inline Plan make_plan(int64_t n, int vec, uint32_t block, uint32_t max_grid_y) {
     Plan P;
     P.nv = (uint32_t)(n / vec);
     P.wide = P.nv >= block;
-    P.rpb = P.wide ? 1u : block / P.nv;
-    P.tiles = P.wide ? (P.nv + block - 1) / block : 1u;
-    P.rows_per_launch = (int64_t)max_grid_y * P.rpb;
+    P.tiles = P.wide ? (P.nv + block - 1) / block : 0u;
+    P.rows_per_launch = P.wide ? (int64_t)max_grid_y : kFlatLanes / P.nv;
     return P;
+}
+
+// Blocks of `block` lanes for `rows` narrow rows of nv vectors.
+inline uint32_t flat_blocks(int64_t rows, uint32_t nv, uint32_t block) {
+    return (uint32_t)((rows * nv + block - 1) / block);
 }
 
 }  // namespace swiglu_host

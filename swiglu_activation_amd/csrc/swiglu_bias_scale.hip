@@ -312,8 +312,7 @@ swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
     const float* sc;
     Geom G;
     G.nv = P.nv;
-    G.rpb = P.rpb;
-    G.inv_nv = 1.0f / (float)P.nv;
+    G.inv_nv = 1.0 / (double)P.nv;
     void* args[] = {&g, &gs, &u, &us, &y, &ys, &bg, &bu, &sc, &scs, &G};
     for (int64_t r0 = 0; r0 < rows; r0 += P.rows_per_launch) {
         const int64_t rc = rows - r0 < P.rows_per_launch ? rows - r0 : P.rows_per_launch;
@@ -322,8 +321,9 @@ swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
         y = const_cast<T*>(static_cast<const T*>(ops[2].p)) + r0 * ys;
         sc = A.scale != nullptr ? A.scale + r0 * scs : nullptr;
         G.rows = rc;
-        const uint32_t groups = (uint32_t)((rc + P.rpb - 1) / P.rpb);
-        if (hipLaunchKernel(k, dim3(P.tiles, groups), dim3(kBlock), args, 0, stream) != hipSuccess)
+        const dim3 grid = P.wide ? dim3(P.tiles, (uint32_t)rc)
+                                 : dim3(swiglu_host::flat_blocks(rc, P.nv, kBlock), 1);
+        if (hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream) != hipSuccess)
             return SWIGLU_ERR_HIP;
     }
     return SWIGLU_OK;

@@ -231,10 +231,15 @@ __device__ __forceinline__ float h_factor_lo(float z, float zlo, float osig) {
 struct Geom {
     int64_t rows;     // rows covered by this launch
     uint32_t nv;      // vectors per half row (n / VEC)
-    uint32_t rpb;     // rows per block (1 when WIDE)
-    float inv_nv;     // 1 / nv (narrow mode)
+    double inv_nv;    // 1 / nv (narrow mode)
 };
 
+// The (row, vector) a lane owns. WIDE: block (x, y) owns vectors
+// [256 x, 256 x + 256) of row y. Narrow: lane L = 256 blockIdx.x + t of the
+// flat launch owns row L / nv, vector L % nv. The quotient is taken as
+// floor((L + 1/2) * fp64(1/nv)): for L < 2^31 and nv < 256 the product is
+// within 2^-21 of (L + 1/2) / nv, whose distance to the nearest integer is at
+// least 1/(2 nv) > 2^-9, so the floor is exact.
 template <bool WIDE>
 __device__ __forceinline__ bool locate(const Geom& G, int64_t& row, uint32_t& col) {
     if constexpr (WIDE) {
@@ -242,11 +247,11 @@ __device__ __forceinline__ bool locate(const Geom& G, int64_t& row, uint32_t& co
         col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
         return col < G.nv;
     } else {
-        const uint32_t t = threadIdx.x;
-        const uint32_t q = (uint32_t)(((float)t + 0.5f) * G.inv_nv);
-        col = t - q * G.nv;
-        row = (int64_t)blockIdx.y * G.rpb + q;
-        return q < G.rpb && row < G.rows;
+        const uint32_t L = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+        const uint32_t q = (uint32_t)(((double)L + 0.5) * G.inv_nv);
+        col = L - q * G.nv;
+        row = q;
+        return (int64_t)q < G.rows;
     }
 }
 

@@ -114,16 +114,15 @@ swiglu_status launch_chunks(const void* kernel, const Plan& P, int64_t rows, con
     }
     args[2 * NOPS] = &G;
     G.nv = P.nv;
-    G.rpb = P.rpb;
-    G.inv_nv = 1.0f / (float)P.nv;
+    G.inv_nv = 1.0 / (double)P.nv;
     for (int64_t r0 = 0; r0 < rows; r0 += P.rows_per_launch) {
         const int64_t rc = rows - r0 < P.rows_per_launch ? rows - r0 : P.rows_per_launch;
         for (int i = 0; i < NOPS; ++i)
             ptr[i] = const_cast<T*>(static_cast<const T*>(ops[i].p)) + r0 * ops[i].stride;
         G.rows = rc;
-        const uint32_t groups = (uint32_t)((rc + P.rpb - 1) / P.rpb);
-        const hipError_t e =
-            hipLaunchKernel(kernel, dim3(P.tiles, groups), dim3(kBlock), args, 0, stream);
+        const dim3 grid = P.wide ? dim3(P.tiles, (uint32_t)rc)
+                                 : dim3(swiglu_host::flat_blocks(rc, P.nv, kBlock), 1);
+        const hipError_t e = hipLaunchKernel(kernel, grid, dim3(kBlock), args, 0, stream);
         if (e != hipSuccess) return SWIGLU_ERR_HIP;
     }
     return SWIGLU_OK;

@@ -39,8 +39,12 @@ int main() {
             long long n; int vec; unsigned block, maxgy;
             std::scanf("%lld %d %u %u", &n, &vec, &block, &maxgy);
             Plan P = make_plan(n, vec, block, maxgy);
-            std::printf("%d %u %u %u %lld\n", P.wide ? 1 : 0, P.nv, P.rpb, P.tiles,
+            std::printf("%d %u %u %lld\n", P.wide ? 1 : 0, P.nv, P.tiles,
                         (long long)P.rows_per_launch);
+        } else if (op == 'f') {
+            long long rows; unsigned nv, block;
+            std::scanf("%lld %u %u", &rows, &nv, &block);
+            std::printf("%u\n", flat_blocks(rows, nv, block));
         }
     }
     return 0;
@@ -129,8 +133,28 @@ def test_vec_bytes(driver):
 def test_launch_plan(driver):
     got = driver(["p 32768 8 256 65535", "p 1792 8 256 65535", "p 11008 4 256 65535",
                   "p 1 1 256 65535", "p 2048 8 256 65535"])
-    assert got[0] == "1 4096 1 16 65535"          # wide: 16 tiles per row
-    assert got[1] == "0 224 1 1 65535"            # narrow: one row of 224 vectors per block
-    assert got[2] == "1 2752 1 11 65535"          # ragged last tile
-    assert got[3] == "0 1 256 1 16776960"         # 256 rows per block
-    assert got[4] == "1 256 1 1 65535"
+    assert got[0] == "1 4096 16 65535"            # wide: 16 tiles per row
+    assert got[1] == f"0 224 0 {2 ** 31 // 224}"   # narrow: flat, at most 2^31 lanes per launch
+    assert got[2] == "1 2752 11 65535"            # ragged last tile
+    assert got[3] == f"0 1 0 {2 ** 31}"
+    assert got[4] == "1 256 1 65535"
+    # flat grid: ceil(rows * nv / 256) blocks, and the largest launch stays below 2^23 blocks
+    got = driver(["f 8192 224 256", "f 1 1 256", "f 3 100 256", f"f {2 ** 31 // 224} 224 256"])
+    assert got == ["7168", "1", "2", str(-(-(2 ** 31 // 224) * 224 // 256))]
+
+
+def test_flat_lane_to_row_division_is_exact():
+    """The narrow-row kernels split a flat lane index L into (row, vector) as
+    floor((L + 1/2) * fp64(1/nv)) and L - row * nv. Checked here in IEEE
+    double (the same arithmetic as the GPU's fp64 ops) for every nv below 256,
+    on lanes around every multiple of nv near 0 and near the top of the
+    largest launch (2^31 / nv rows, plus one block of overshoot)."""
+    import numpy as np
+    for nv in range(1, 256):
+        inv = 1.0 / nv
+        top = (2 ** 31 // nv) * nv + 255
+        ks = np.concatenate([np.arange(0, 64), np.arange(top // nv - 64, top // nv + 2)])
+        L = (ks[:, None] * nv + np.arange(-2, 3)[None, :]).ravel()
+        L = L[(L >= 0) & (L <= top)].astype(np.uint64)
+        q = np.floor((L.astype(np.float64) + 0.5) * inv).astype(np.uint64)
+        assert np.array_equal(q, L // nv), nv
