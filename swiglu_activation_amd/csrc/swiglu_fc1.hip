@@ -53,6 +53,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_XCD
 #define SWIGLU_FC_XCD 0         // give each XCD a contiguous range of the launch order
 #endif
+#ifndef SWIGLU_FC_NT_EPI
+#define SWIGLU_FC_NT_EPI 0      // nontemporal hint on the epilogue's stores
+#endif
 #ifndef SWIGLU_FC_CPOL
 #define SWIGLU_FC_CPOL 0        // cache-policy bits of the copies (gfx950: 1 sc0, 2 nt)
 #endif
@@ -189,6 +192,24 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// Four fp32 values rounded to bf16 (nearest even) and stored as 8 bytes.
+// A lane's four values are 16 bytes apart from its neighbours' in the row,
+// so whole cache lines form only in L2: the stores carry no nontemporal
+// hint (which would send the partial lines on to memory unmerged).
+__device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
+    uint32_t w[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        f32x2 pr = {v[2 * i], v[2 * i + 1]};
+        w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+    }
+#if SWIGLU_FC_NT_EPI
+    __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(p));
+#else
+    *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
+#endif
 }
 
 __device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
@@ -423,10 +444,10 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
                     sigmoid_pair<uint16_t, false>(gv[r], sig, osig);
                     yv[r] = (gv[r] * sig) * uv[r];
                 }
-                Vec<uint16_t, 4>::store(P.y + tok * P.ldy + f, yv);
+                store4(P.y + tok * P.ldy + f, yv);
                 if (P.x != nullptr) {
-                    Vec<uint16_t, 4>::store(P.x + tok * P.ldx + f, gv);
-                    Vec<uint16_t, 4>::store(P.x + tok * P.ldx + P.n + f, uv);
+                    store4(P.x + tok * P.ldx + f, gv);
+                    store4(P.x + tok * P.ldx + P.n + f, uv);
                 }
             }
         }
