@@ -53,6 +53,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_XCD
 #define SWIGLU_FC_XCD 0         // give each XCD a contiguous range of the launch order
 #endif
+#ifndef SWIGLU_FC_LDS_EPI
+#define SWIGLU_FC_LDS_EPI 1     // stage the epilogue through LDS for whole-line stores
+#endif
 #ifndef SWIGLU_FC_NT_EPI
 #define SWIGLU_FC_NT_EPI 0      // nontemporal hint on the epilogue's stores
 #endif
@@ -301,6 +304,52 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t f_tiles, uint32_t t
     ft = in / gs;
 }
 
+// Epilogue staging: a wave's tile (128 tokens x 64 features of one output)
+// in LDS rows of 72 bf16 (144 bytes, 16-byte aligned rows).
+constexpr int kEpiPitch = kFcWaveF + 8;
+constexpr int kEpiRegion = kFcWaveT * kEpiPitch;
+static_assert(!SWIGLU_FC_LDS_EPI || (kFcWaves == 4 && 2 * kEpiRegion <= kFcStageElems),
+              "two waves' regions per stage, in stages 0 and 1");
+
+// Writes the wave's 128 x 64 tile of one output, value(i, j, e) for
+// accumulator element e of MFMA tile (feature i, token j), to out (row
+// stride ld) at token tw, feature fw, skipping tokens >= m and features >= n.
+// Register e of a 32x32 tile holds feature (e % 4) + 8 (e / 4) + 4 (lane / 32)
+// and token lane % 32.
+template <typename V>
+__device__ __forceinline__ void epi_out(uint16_t* region, int64_t tw, int64_t fw, int64_t m,
+                                        int64_t n, uint16_t* out, int64_t ld, V value) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kFcMF; ++i)
+#pragma unroll
+        for (int j = 0; j < kFcMT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = value(i, j, 4 * q + r);
+                uint32_t w[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    f32x2 pr = {v[2 * h], v[2 * h + 1]};
+                    w[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+                }
+                const int row = 32 * j + lane % 32, col = 32 * i + 8 * q + 4 * (lane / 32);
+                *reinterpret_cast<u32x2*>(region + row * kEpiPitch + col) = u32x2{w[0], w[1]};
+            }
+    // back by rows: lane l takes 16 bytes (8 features) of row 8 it + l / 8
+    constexpr int kChunks = kFcWaveF / 8;             // 16-byte chunks per tile row
+    constexpr int kRowsPerPass = 64 / kChunks;
+#pragma unroll
+    for (int it = 0; it < kFcWaveT / kRowsPerPass; ++it) {
+        const int row = kRowsPerPass * it + lane / kChunks, col = 8 * (lane % kChunks);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(region + row * kEpiPitch + col);
+        const int64_t tok = tw + row, f = fw + col;
+        if (tok < m && f < n) *reinterpret_cast<u32x4*>(out + tok * ld + f) = v;
+    }
+}
+
 struct Ctx {
     Sources src;
     int wt, wf;
@@ -422,6 +471,26 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     // No copy may still be writing LDS when the workgroup ends.
     wait_copies_and_lds<0>();
 
+#if SWIGLU_FC_LDS_EPI
+    // Epilogue through LDS (free now): every wave writes its tile of each
+    // output into a private LDS region in registers' order, then reads it
+    // back by rows, so each store instruction writes 8 rows of 128 bytes.
+    ring_barrier();                                   // every wave is done with the stages
+    uint16_t* region = (wave < 2 ? stage<0>() : stage<1>()) + (wave & 1) * kEpiRegion;
+    const int64_t tw = t0 + c.wt, fw = f0 + c.wf;     // the wave's first token and feature
+    epi_out(region, tw, fw, P.m, P.n, P.y, P.ldy, [&](int i, int j, int e) {
+        const float g = acc.g[i][j][e];
+        float sig, osig;
+        sigmoid_pair<uint16_t, false>(g, sig, osig);
+        return (g * sig) * acc.u[i][j][e];
+    });
+    if (P.x != nullptr) {
+        epi_out(region, tw, fw, P.m, P.n, P.x, P.ldx,
+                [&](int i, int j, int e) { return acc.g[i][j][e]; });
+        epi_out(region, tw, fw, P.m, P.n, P.x + P.n, P.ldx,
+                [&](int i, int j, int e) { return acc.u[i][j][e]; });
+    }
+#else
     // Epilogue. Register v of a 32x32 tile holds feature
     // (v % 4) + 8 (v / 4) + 4 (lane / 32) and token lane % 32, so each group
     // of four registers is four consecutive features of one token.
@@ -451,6 +520,7 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
                 }
             }
         }
+#endif
 }
 
 }  // namespace
