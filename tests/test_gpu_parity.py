@@ -242,3 +242,34 @@ def test_runs_on_the_callers_stream():
     sw.swiglu_gateup_fwd(x, y2, stream=s)
     s.synchronize()
     assert gu.bits_equal(y2, ref_y)
+
+
+@pytest.mark.parametrize("rows,n", [(65535 + 100, 2048), (800_003, 200)])
+def test_launch_chunks_and_large_flat_index(rows, n):
+    """Wide rows past 65535 (the forward and backward split into two
+    launches), and narrow rows whose flat lane index passes 2^24 (an fp32
+    quotient would no longer be exact there). Inputs are drawn on the device
+    (seeded torch generator, rounded to bf16); rows around the launch
+    boundary, the last rows and a random sample are compared with the
+    oracle; the in-place backward must equal the out-of-place one bitwise."""
+    _say(f"[chunks] rows={rows} n={n}")
+    gen = torch.Generator(device="cuda").manual_seed(rows + n)
+    x = (torch.randn(rows, 2 * n, device="cuda", generator=gen) * 2).bfloat16()
+    dy = torch.randn(rows, n, device="cuda", generator=gen).bfloat16()
+    y = sw.swiglu_gateup_fwd(x)
+    dx = sw.swiglu_gateup_bwd(dy, x)
+    xi = x.clone()
+    sw.swiglu_gateup_bwd(dy, xi, in_place=True)
+    torch.cuda.synchronize()
+    assert gu.bits_equal(xi, dx)
+    rng = np.random.default_rng(rows)
+    pick = np.unique(np.concatenate([np.arange(0, 4), np.arange(65530, 65541),
+                                     np.arange(rows - 4, rows), rng.choice(rows, 64, replace=False)]))
+    pick = pick[pick < rows]
+    idx = torch.from_numpy(pick).cuda()
+    x_h, dy_h = gu.from_dev(x[idx]), gu.from_dev(dy[idx])
+    xf, dyf = oracle.widen(x_h, "bf16"), oracle.widen(dy_h, "bf16")
+    st = {"fwd": gu.compare(gu.from_dev(y[idx]), oracle.oracle_fwd(xf), "bf16", "fwd"),
+          "bwd": gu.compare(gu.from_dev(dx[idx]), oracle.oracle_bwd(xf, dyf), "bf16", "bwd")}
+    del x, dy, y, dx, xi
+    _assert_stats(st)
