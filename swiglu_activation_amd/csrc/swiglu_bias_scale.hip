@@ -41,7 +41,27 @@ __device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
     e = (a - (s - bb)) + (b - bb);
 }
 
-template <typename T, int VEC, bool WIDE>
+// Widens VEC elements of T held as raw bits (as Vec<T, VEC>::load does
+// after its load).
+template <typename T, int VEC>
+__device__ __forceinline__ void widen_bits(typename Vec<T, VEC>::R r, float (&f)[VEC]) {
+    constexpr int kBytes = Vec<T, VEC>::kBytes;
+    if constexpr (sizeof(T) == 4) {
+        __builtin_memcpy(f, &r, sizeof(r));
+    } else if constexpr (kBytes == 2) {
+        f[0] = __uint_as_float((uint32_t)r << 16);
+    } else {
+        uint32_t w[kBytes / 4];
+        __builtin_memcpy(w, &r, sizeof(r));
+#pragma unroll
+        for (int i = 0; i < kBytes / 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);           // lower address: low half
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+
+template <typename T, int VEC, bool WIDE, bool HAS_BIAS, bool HAS_SCALE>
 __global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
     const T* __restrict__ gp, int64_t gs, const T* __restrict__ up, int64_t us,
     T* __restrict__ y, int64_t ys, const T* __restrict__ bg, const T* __restrict__ bu,
@@ -50,25 +70,35 @@ __global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
     uint32_t col;
     if (!locate<WIDE>(G, row, col)) return;
     const int64_t c = (int64_t)col * VEC;
+    // Every load is issued before any is used (bias and scale are compile-
+    // time options, so there is no branch between them).
+    typedef typename Vec<T, VEC>::R R;
+    const R gr = load_raw<R>(gp + row * gs + c);
+    const R ur = load_raw<R>(up + row * us + c);
+    R bgr{}, bur{};
+    if constexpr (HAS_BIAS) {
+        bgr = *reinterpret_cast<const R*>(bg + c);     // re-read by every row: cached
+        bur = *reinterpret_cast<const R*>(bu + c);
+    }
+    const float s = HAS_SCALE ? sc[row * scs] : 1.0f;
     float g[VEC], u[VEC], out[VEC];
-    Vec<T, VEC>::load(gp + row * gs + c, g);
-    Vec<T, VEC>::load(up + row * us + c, u);
-    if (bg != nullptr) {
+    widen_bits<T, VEC>(gr, g);
+    widen_bits<T, VEC>(ur, u);
+    if constexpr (HAS_BIAS) {
         float b[VEC], d[VEC];
-        Vec<T, VEC>::template load<true>(bg + c, b);
-        Vec<T, VEC>::template load<true>(bu + c, d);
+        widen_bits<T, VEC>(bgr, b);
+        widen_bits<T, VEC>(bur, d);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
             g[i] += b[i];
             u[i] += d[i];
         }
     }
-    const float s = sc != nullptr ? sc[row * scs] : 1.0f;
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
         float sig, osig;
         sigmoid_pair<T, false>(g[i], sig, osig);
-        out[i] = ((g[i] * sig) * u[i]) * s;
+        out[i] = HAS_SCALE ? ((g[i] * sig) * u[i]) * s : (g[i] * sig) * u[i];
     }
     Vec<T, VEC>::store(y + row * ys + c, out);
 }
@@ -107,26 +137,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
     v += dpp_f<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
-// Widens VEC elements of T held as raw bits (as Vec<T, VEC>::load does
-// after its load).
-template <typename T, int VEC>
-__device__ __forceinline__ void widen_bits(typename Vec<T, VEC>::R r, float (&f)[VEC]) {
-    constexpr int kBytes = Vec<T, VEC>::kBytes;
-    if constexpr (sizeof(T) == 4) {
-        __builtin_memcpy(f, &r, sizeof(r));
-    } else if constexpr (kBytes == 2) {
-        f[0] = __uint_as_float((uint32_t)r << 16);
-    } else {
-        uint32_t w[kBytes / 4];
-        __builtin_memcpy(w, &r, sizeof(r));
-#pragma unroll
-        for (int i = 0; i < kBytes / 4; ++i) {
-            f[2 * i] = __uint_as_float(w[i] << 16);           // lower address: low half
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
 }
 
 template <typename T, int VEC, bool IN_PLACE>
@@ -297,12 +307,24 @@ struct BsArgs {
     int64_t scale_stride;
 };
 
+template <typename T, int VEC, bool WIDE>
+const void* fwd_bs_kernel_for(bool has_bias, bool has_scale) {
+    if (has_bias)
+        return has_scale
+                   ? reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, WIDE, true, true>)
+                   : reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, WIDE, true, false>);
+    return has_scale
+               ? reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, WIDE, false, true>)
+               : reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, WIDE, false, false>);
+}
+
 template <typename T, int VEC>
 swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, int64_t n,
                             hipStream_t stream) {
     const Plan P = make_plan(n, VEC);
-    const void* k = P.wide ? reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, true>)
-                           : reinterpret_cast<const void*>(&swiglu_fwd_bs_kernel<T, VEC, false>);
+    const bool hb = A.bias != nullptr, hs = A.scale != nullptr;
+    const void* k = P.wide ? fwd_bs_kernel_for<T, VEC, true>(hb, hs)
+                           : fwd_bs_kernel_for<T, VEC, false>(hb, hs);
     const T* g;
     const T* u;
     T* y;
