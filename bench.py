@@ -206,11 +206,28 @@ def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
         if k >= 2:
             bt.append((a.elapsed_time(b), b.elapsed_time(c)))
     bf, bb = float(np.mean([t[0] for t in bt])), float(np.mean([t[1] for t in bt]))
+    # the routed-expert form: a per-token scale and no bias, dx and dscale
+    st = []
+    for k in range(iters + 2):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        sw.swiglu_gateup_bias_scale_fwd(x, None, scale_t, y)
+        b.record(stream)
+        sw.swiglu_gateup_bias_scale_bwd(dy, x, None, scale_t, dx, workspace=ws)
+        c.record(stream)
+        c.synchronize()
+        if k >= 2:
+            st.append((a.elapsed_time(b), b.elapsed_time(c)))
+    sf, sb = float(np.mean([t[0] for t in st])), float(np.mean([t[1] for t in st]))
     return {"fwd_ms": round(bf, 5), "bwd_ms": round(bb, 5),
             "fwd_GBps": round(fwd_bytes / bf / 1e6, 1),
             "bwd_GBps": round(bwd_bytes / bb / 1e6, 1),
             "what": "z = x + bias, y = s * silu(z_g) * z_u; bwd writes dx, dbias, "
-                    "dscale (GB/s on the base op's bytes)"}
+                    "dscale (GB/s on the base op's bytes)",
+            "scale_only": {"fwd_ms": round(sf, 5), "bwd_ms": round(sb, 5),
+                           "fwd_GBps": round(fwd_bytes / sf / 1e6, 1),
+                           "bwd_GBps": round(bwd_bytes / sb / 1e6, 1),
+                           "what": "no bias, per-token scale; bwd writes dx and dscale"}}
 
 
 def configs_leg(dev, stream, skip: str, replays: int = 10):

@@ -28,6 +28,9 @@ using namespace swiglu_impl;
 #ifndef SWIGLU_BS_PREFETCH
 #define SWIGLU_BS_PREFETCH 1           // load the next row while computing this one (backward)
 #endif
+#ifndef SWIGLU_BS_ONE_SHOT
+#define SWIGLU_BS_ONE_SHOT 1           // backward without dbias on wide rows: one-shot grid
+#endif
 #ifndef SWIGLU_BS_INTERLEAVE
 #define SWIGLU_BS_INTERLEAVE 1         // group y takes rows y, y+G, y+2G, ... (else a band)
 #endif
@@ -139,6 +142,26 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// One element of the backward: z = x + bias (the gate carried as a two-sum,
+// so the root series sees the sum's rounding error), dz for gate and up, and
+// the element's term dy * silu(z_g) * z_u added to p (for dscale). Shared by
+// the row-loop and one-shot kernels so that both give the same bits.
+template <typename T>
+__device__ __forceinline__ void bwd_bs_elem(float g, float u, float d, float bg, float bu, float s,
+                                            float& dg, float& du, float& p) {
+    float zg, zlo;
+    two_sum(g, bg, zg, zlo);
+    const float zu = u + bu;
+    float sig, osig;
+    sigmoid_pair<T, true>(zg, sig, osig);
+    const float h = h_factor_lo<T>(zg, zlo, osig);
+    const float silu = zg * sig;
+    const float ds_ = d * s;
+    du = ds_ * silu;
+    dg = ((ds_ * zu) * sig) * h;
+    p = __builtin_fmaf(d * silu, zu, p);
+}
+
 template <typename T, int VEC, bool IN_PLACE>
 __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs_kernel(
     const T* dyp, int64_t dys, T* gp, int64_t gs, T* up, int64_t us, T* dgp, int64_t dgs,
@@ -182,17 +205,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs_kernel(
             float dg[VEC], du[VEC];
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
-                float zg, zlo;
-                two_sum(g[i], bgv[i], zg, zlo);
-                const float zu = u[i] + buv[i];
-                float sig, osig;
-                sigmoid_pair<T, true>(zg, sig, osig);
-                const float h = h_factor_lo<T>(zg, zlo, osig);
-                const float silu = zg * sig;
-                const float ds_ = d[i] * s;
-                du[i] = ds_ * silu;
-                dg[i] = ((ds_ * zu) * sig) * h;
-                p = __builtin_fmaf(d[i] * silu, zu, p);
+                bwd_bs_elem<T>(g[i], u[i], d[i], bgv[i], buv[i], s, dg[i], du[i], p);
                 acc_g[i] += dg[i];
                 acc_u[i] += du[i];
             }
@@ -266,6 +279,60 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs_kernel(
             pg[i] = acc_g[i];
             pg[G.n + i] = acc_u[i];
         }
+    }
+}
+
+// The backward without dbias on wide rows (at least 256 vectors per half
+// row): a one-shot grid like the base backward, block (x, y) = column tile x
+// of row y. dscale partials, when wanted, are written exactly as the row-loop
+// kernel writes them (same lanes, same wave sums), so the results are the
+// same bits either way.
+template <typename T, int VEC, bool IN_PLACE, bool HAS_BIAS, bool HAS_SCALE, bool WANT_DS>
+__global__ __launch_bounds__(kBlock) void swiglu_bwd_bs1_kernel(
+    const T* dyp, int64_t dys, T* gp, int64_t gs, T* up, int64_t us, T* dgp, int64_t dgs,
+    T* dup, int64_t dus, const T* __restrict__ bg, const T* __restrict__ bu,
+    const float* __restrict__ sc, int64_t scs, float* part_ds, BsGeom G) {
+    if constexpr (IN_PLACE) {
+        dgp = gp;
+        dgs = gs;
+        dup = up;
+        dus = us;
+    }
+    const int64_t row = blockIdx.y;
+    const uint32_t col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+    const bool active = col < G.nv;
+    if (!WANT_DS && !active) return;
+    const int64_t c = (int64_t)col * VEC;
+    typedef typename Vec<T, VEC>::R R;
+    R gr{}, ur{}, dr{}, bgr{}, bur{};
+    if (active) {
+        gr = load_raw<R>(gp + row * gs + c);
+        ur = load_raw<R>(up + row * us + c);
+        dr = load_raw<R>(dyp + row * dys + c);
+        if constexpr (HAS_BIAS) {
+            bgr = *reinterpret_cast<const R*>(bg + c);   // re-read by every row: cached
+            bur = *reinterpret_cast<const R*>(bu + c);
+        }
+    }
+    const float s = HAS_SCALE ? sc[row * scs] : 1.0f;
+    float p = 0.0f;
+    if (active) {
+        float g[VEC], u[VEC], d[VEC], b[VEC], e[VEC], dg[VEC], du[VEC];
+        widen_bits<T, VEC>(gr, g);
+        widen_bits<T, VEC>(ur, u);
+        widen_bits<T, VEC>(dr, d);
+        widen_bits<T, VEC>(bgr, b);                     // zero bits when there is no bias
+        widen_bits<T, VEC>(bur, e);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) bwd_bs_elem<T>(g[i], u[i], d[i], b[i], e[i], s, dg[i], du[i], p);
+        Vec<T, VEC>::store(dgp + row * dgs + c, dg);
+        Vec<T, VEC>::store(dup + row * dus + c, du);
+    }
+    if constexpr (WANT_DS) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const float w = wave_sum(p);
+        if (lane == 0)
+            part_ds[((int64_t)blockIdx.x * kWaves + wave) * G.total_rows + G.row0 + row] = w;
     }
 }
 
@@ -386,6 +453,23 @@ swiglu_status sum_partials(const float* part, int64_t count, int64_t jstride, in
                : SWIGLU_ERR_HIP;
 }
 
+// The one-shot backward for the given options (16-byte vectors only).
+template <typename T, int VEC>
+const void* bwd_bs1_kernel_for(bool in_place, bool has_bias, bool has_scale, bool want_ds) {
+    if constexpr (VEC * sizeof(T) != 16) {
+        return nullptr;
+    } else {
+#define SWIGLU_BS1(IP, B, S, D) reinterpret_cast<const void*>(&swiglu_bwd_bs1_kernel<T, VEC, IP, B, S, D>)
+#define SWIGLU_BS1_S(IP, B) \
+    (!has_scale ? SWIGLU_BS1(IP, B, false, false) \
+                : want_ds ? SWIGLU_BS1(IP, B, true, true) : SWIGLU_BS1(IP, B, true, false))
+        if (in_place) return has_bias ? SWIGLU_BS1_S(true, true) : SWIGLU_BS1_S(true, false);
+        return has_bias ? SWIGLU_BS1_S(false, true) : SWIGLU_BS1_S(false, false);
+#undef SWIGLU_BS1_S
+#undef SWIGLU_BS1
+    }
+}
+
 // ops: dy, gate, up, dgate, dup.
 template <typename T, int VEC>
 swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, int64_t n,
@@ -416,9 +500,18 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
     G.nv = nv;
     G.tiles = tiles;
     G.total_rows = rows;
+    // Without dbias, wide rows of 16-byte vectors take the one-shot kernel
+    // (the row loop exists for the dbias column sums).
+    const bool one_shot = SWIGLU_BS_ONE_SHOT && dbias == nullptr && nv >= (uint32_t)kBlock &&
+                          VEC * sizeof(T) == 16;
     void* args[] = {&dyp, &dys, &gp, &gs, &upp, &us, &dgp, &dgs, &dup, &dus,
                     &bg, &bu, &sc, &scs, &part_db, &part_ds, &G};
-    const int64_t rows_per_launch = (int64_t)kMaxGridY * kBsRows;
+    void* args1[] = {&dyp, &dys, &gp, &gs, &upp, &us, &dgp, &dgs, &dup, &dus,
+                     &bg, &bu, &sc, &scs, &part_ds, &G};
+    const void* k1 = one_shot ? bwd_bs1_kernel_for<T, VEC>(in_place, bg != nullptr,
+                                                           A.scale != nullptr, dscale != nullptr)
+                              : nullptr;
+    const int64_t rows_per_launch = one_shot ? (int64_t)kMaxGridY : (int64_t)kMaxGridY * kBsRows;
     for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
         const int64_t rc = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
         dyp = static_cast<const T*>(ops[0].p) + r0 * dys;
@@ -430,6 +523,12 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
         G.rows = rc;
         G.row0 = r0;
         G.group0 = r0 / kBsRows;
+        if (one_shot) {
+            if (hipLaunchKernel(k1, dim3(tiles, (uint32_t)rc), dim3(kBlock), args1, 0, stream) !=
+                hipSuccess)
+                return SWIGLU_ERR_HIP;
+            continue;
+        }
         const uint32_t gy = (uint32_t)bs_groups(rc);
         if (hipLaunchKernel(k, dim3(tiles, gy), dim3(kBlock), args, 0, stream) != hipSuccess)
             return SWIGLU_ERR_HIP;

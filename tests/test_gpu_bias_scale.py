@@ -200,3 +200,37 @@ def test_full_size_workloads_with_bias_and_scale(name):
     x_h, dy_h = synth.make_x(w), synth.make_dy(w)
     _, _, b_h, s_h = _make(w.rows, w.n, w.dtype, seed=46, x_h=x_h, dy_h=dy_h)
     _run_and_check(x_h, dy_h, b_h, s_h, w.dtype, in_place=w.in_place, shape=w.shape)
+
+
+@pytest.mark.parametrize("dtype,n", [("bf16", 2048), ("fp32", 1024)])
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_one_shot_backward_matches_row_loop(dtype, n, bias, in_place):
+    """Without dbias, wide rows of 16-byte vectors take a one-shot kernel;
+    with dbias, the row-loop kernel. dx and dscale must be the same bits."""
+    print(f"[bias/scale one-shot] {dtype} n={n} bias={bias} in_place={in_place}", flush=True)
+    x_h, dy_h, b_h, s_h = _make(515, n, dtype, seed=47, bias=bias, scale=True)
+    x, dy = gu.to_dev(x_h, dtype), gu.to_dev(dy_h, dtype)
+    b = gu.to_dev(b_h, dtype) if bias else None
+    s = torch.from_numpy(s_h).cuda()
+    ref_b = gu.to_dev(b_h, dtype) if bias else gu.to_dev(np.zeros(2 * n, x_h.dtype), dtype)
+    # row loop (dbias requested; a zero bias when the case has none)
+    dx_l, _, ds_l = sw.swiglu_gateup_bias_scale_bwd(dy, x.clone(), ref_b, s, want_dbias=True,
+                                                    in_place=in_place)
+    # one shot
+    dx_o, db_o, ds_o = sw.swiglu_gateup_bias_scale_bwd(dy, x.clone(), b, s, want_dbias=False,
+                                                       in_place=in_place)
+    torch.cuda.synchronize()
+    assert db_o is None
+    assert gu.bits_equal(dx_l, dx_o)
+    assert torch.equal(ds_l.view(torch.int32), ds_o.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_scale_only_wide_rows_parity(dtype):
+    """The per-token-scale form without a bias (routed experts) on wide rows:
+    the one-shot backward against the oracle."""
+    print(f"[bias/scale scale only] {dtype}", flush=True)
+    x_h, dy_h, b_h, s_h = _make(300, 4096, dtype, seed=48, bias=False, scale=True)
+    _run_and_check(x_h, dy_h, b_h, s_h, dtype)
+    _run_and_check(x_h, dy_h, b_h, s_h, dtype, in_place=True)
