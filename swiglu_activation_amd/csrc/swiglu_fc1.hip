@@ -59,6 +59,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_NT_EPI
 #define SWIGLU_FC_NT_EPI 0      // nontemporal hint on the epilogue's stores
 #endif
+#ifndef SWIGLU_FC_COPYMAP
+#define SWIGLU_FC_COPYMAP 0     // 1: each wave copies a contiguous band of rows
+#endif
 #ifndef SWIGLU_FC_CPOL
 #define SWIGLU_FC_CPOL 0        // cache-policy bits of the copies (gfx950: 1 sc0, 2 nt)
 #endif
@@ -138,10 +141,20 @@ __device__ __forceinline__ int chunk_slot(int r, int c) {
     else return c ^ ((r >> 1) & 7);
 }
 
-// Source row of each of this thread's copies, at k = 0. Copy i of wave v
-// fills LDS rows [16 q, 16 q + 16) of a stage, q = i * waves + v; lane l
-// writes slot l % 4 of row 16 q + l / 4, so it reads the chunk that belongs
-// in that slot.
+// The block of kFcCopyRows LDS rows that copy i of a wave fills: the waves
+// interleave block by block (COPYMAP 0) or each takes a contiguous band.
+__device__ __forceinline__ int copy_block(int i, int wave) {
+#if SWIGLU_FC_COPYMAP
+    return wave * kFcCopies + i;
+#else
+    return i * kFcWaves + wave;
+#endif
+}
+
+// Source row of each of this thread's copies, at k = 0. Copy i of a wave
+// fills LDS rows [R q, R q + R) of a stage, R = kFcCopyRows and
+// q = copy_block(i, wave); lane l writes slot l % kFcChunks of row
+// R q + l / kFcChunks, so it reads the chunk that belongs in that slot.
 struct Sources {
     const uint16_t* p[kFcCopies];
 };
@@ -151,7 +164,7 @@ __device__ __forceinline__ void make_sources(const Fc1Args& P, int64_t t0, int64
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kFcCopies; ++i) {
-        const int r = (i * kFcWaves + wave) * kFcCopyRows + lane / kFcChunks;
+        const int r = copy_block(i, wave) * kFcCopyRows + lane / kFcChunks;
         const int c = chunk_slot(r, lane % kFcChunks);
         if (r < kFcRowsA) {
             const int64_t tok = t0 + r < P.m ? t0 + r : P.m - 1;
@@ -170,7 +183,7 @@ __device__ __forceinline__ void copy_tile(const Sources& src, int t) {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kFcCopies; ++i) {
-        uint16_t* dst = stage<S>() + (i * kFcWaves + wave) * kFcCopyRows * kFcRowElems;
+        uint16_t* dst = stage<S>() + copy_block(i, wave) * kFcCopyRows * kFcRowElems;
         __builtin_amdgcn_global_load_lds(
             static_cast<const void*>(src.p[i] + (int64_t)t * kFcTileK),
             (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
