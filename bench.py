@@ -167,6 +167,10 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
         mm = timed(lambda: torch.matmul(a, wt.t(), out=xbuf))
         unfused = timed(lambda: (torch.matmul(a, wt.t(), out=xbuf), sw.swiglu_gateup_fwd(xbuf, y)))
         out[f"tokens{tokens}_hidden{hidden}_n{n}"] = {
+            "roofline": {"bound": "mfma", "kernel": "swiglu_fc1_kernel",
+                         "achieved": round(flops / fused / 1e9, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(flops / fused / 1e9 / PEAK_BF16_TFLOPS, 4),
+                         "flops_per_launch": flops},
             "fused_ms": round(fused, 4), "fused_TFLOPs": round(flops / fused / 1e9, 1),
             "fused_frac_of_peak": round(flops / fused / 1e9 / PEAK_BF16_TFLOPS, 4),
             "fused_with_x_ms": round(fused_x, 4),
