@@ -19,6 +19,8 @@ SRCS = [os.path.join(PKG_DIR, "csrc", "swiglu_gateup.hip"),
         os.path.join(PKG_DIR, "csrc", "swiglu_fc1.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libswiglu_gateup.so")
+CLIENT_SRC = os.path.join(PKG_DIR, "examples", "c_abi_client.c")
+CLIENT = os.path.join(PKG_DIR, "c_abi_client")       # a plain C program using the C ABI
 ARCH = "gfx950"
 
 
@@ -52,7 +54,26 @@ def build(verbose: bool = False) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    build_client(verbose)
     return LIB
+
+
+def build_client(verbose: bool = False) -> str:
+    """Compile the plain C client (C11, host compiler) against the library."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the C ABI client")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), "-o", CLIENT, CLIENT_SRC,
+           "-L", PKG_DIR, "-lswiglu_gateup", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C client build failed ({res.returncode}):\n{res.stderr}")
+    return CLIENT
 
 
 if __name__ == "__main__":
