@@ -87,7 +87,38 @@ def cpu_baseline(w, x_h, dy_h, seconds: float):
             "seconds": round(dt, 3),
             "sample": f"rows 0..{rows} of {w.rows} ({rows * w.n} gate/up pairs) of {w.name}: "
                       "widen to float64, forward, backward (numpy, one thread)",
+            "all_cores": cpu_baseline_all_cores(w, x_h, dy_h),
             "other_rows": cpu_baseline_other_rows(w, x_h, dy_h)}
+
+
+def cpu_baseline_all_cores(w, x_h, dy_h, block: int = 32, max_threads: int = 16):
+    """The same oracle over the whole workload, split by row blocks over a
+    pool of threads, one per core this process may run on (at most
+    `max_threads`). numpy drops the GIL inside its array loops, so the blocks
+    run in parallel; threads rather than processes keep the GPU-initialised
+    process from being forked."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    threads = max(1, min(len(os.sched_getaffinity(0)), max_threads))
+
+    def one(r0):
+        r1 = min(r0 + block, w.rows)
+        xf = oracle.widen(x_h[r0:r1], w.dtype)
+        dyf = oracle.widen(dy_h[r0:r1], w.dtype)
+        y = oracle.oracle_fwd(xf)
+        dx = oracle.oracle_bwd(xf, dyf)
+        return y.shape == (r1 - r0, w.n) and dx.shape == (r1 - r0, 2 * w.n)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        ok = all(pool.map(one, range(0, w.rows, block)))
+    dt = time.perf_counter() - t0
+    assert ok
+    return {"value": round(8 * w.elem_bytes * w.rows * w.n / dt / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "seconds": round(dt, 3),
+            "sample": f"all {w.rows} rows of {w.name}, {block}-row blocks over {threads} threads"}
 
 
 def cpu_baseline_other_rows(w, x_h, dy_h, rows: int = 512):
