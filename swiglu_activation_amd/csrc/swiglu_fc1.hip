@@ -34,6 +34,9 @@
 //  * The next k step's fragments are read while the current step's MFMAs
 //    run; one barrier per tile hands a filled stage to the readers and an
 //    emptied one to the copies.
+//  * The copies of a tile are spread thinly over two k steps (one every two
+//    MFMAs), not issued in a burst: a burst fills the copy queue, and the
+//    wave, which issues in order, then stalls in front of its next MFMA.
 //  * Rows past m (tokens) or n (features) are clamped to the last valid row:
 //    they copy real data, which reaches only accumulators that are never
 //    stored.
@@ -68,6 +71,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_SCHED
 #define SWIGLU_FC_SCHED 1       // pin the interleaving of MFMAs and memory instructions
 #endif
+#ifndef SWIGLU_FC_SPREAD
+#define SWIGLU_FC_SPREAD 2      // copy issue: 0 packed early in the step after the barrier; N >= 1
+#endif                          // spread evenly over that step and the next N - 1 steps
 
 constexpr int kFcWaveT = 128;                        // tokens per wave
 constexpr int kFcWaveF = 64;                         // features per wave (gate and up each)
@@ -96,6 +102,10 @@ constexpr int kFcCopies = kFcRows / kFcCopyRows / kFcWaves;   // copies per thre
 constexpr int kFcMfma = 2 * kFcMF * kFcMT;           // MFMAs per wave per k step
 constexpr int kFcReads = kFcMT + 2 * kFcMF;          // fragment reads per k step
 constexpr int kFcSteps = kFcTileK / 16;              // MFMA k steps per stage
+constexpr int kFcSpread = SWIGLU_FC_SPREAD > 0 ? SWIGLU_FC_SPREAD : 1;   // steps a tile's copies span
+static_assert(kFcSpread <= kFcSteps - 1, "a tile's copies are all issued before the next wait");
+// First copy issued in step j of the span (j = 0: the step after the barrier).
+constexpr int copy_begin(int j) { return j * kFcCopies / kFcSpread; }
 static_assert(kFcTileK == 32 || kFcTileK == 64, "4 or 8 chunks per row");
 static_assert(kFcSteps % 2 == 0, "fragment sets alternate within a stage");
 static_assert(kFcCopies * kFcWaves * kFcCopyRows == kFcRows, "whole copies per stage");
@@ -177,12 +187,12 @@ __device__ __forceinline__ void make_sources(const Fc1Args& P, int64_t t0, int64
     }
 }
 
-// Starts the copies of k tile t into stage S.
-template <int S>
+// Starts copies [I0, I1) of k tile t into stage S.
+template <int S, int I0 = 0, int I1 = kFcCopies>
 __device__ __forceinline__ void copy_tile(const Sources& src, int t) {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kFcCopies; ++i) {
+    for (int i = I0; i < I1; ++i) {
         uint16_t* dst = stage<S>() + copy_block(i, wave) * kFcCopyRows * kFcRowElems;
         __builtin_amdgcn_global_load_lds(
             static_cast<const void*>(src.p[i] + (int64_t)t * kFcTileK),
@@ -292,6 +302,20 @@ __device__ __forceinline__ void sched_copies_reads_among_mfma() {
     }
     __builtin_amdgcn_sched_group_barrier(kSgMfma, kFcMfma - kFcReads, 0);
     __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+// NC copies spread evenly over the step's MFMAs, the fragment reads after
+// the first kFcReads of them.
+template <int NC, int M = 0>
+__device__ __forceinline__ void sched_mix_at() {
+#if SWIGLU_FC_SCHED
+    constexpr int nc = (M + 1) * NC / kFcMfma - M * NC / kFcMfma;
+    if constexpr (nc > 0) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, nc, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if constexpr (M < kFcReads) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    if constexpr (M + 1 < kFcMfma) sched_mix_at<NC, M + 1>();
+    else __builtin_amdgcn_sched_barrier(0);
 #endif
 }
 
@@ -405,22 +429,47 @@ __device__ __forceinline__ void inner_step(const Ctx& c, bool live, Frags& C, Fr
     sched_reads_among_mfma();
 }
 
+// inner_step that also issues copies [I0, I1) of slot ts into stage SP,
+// spread over the step's MFMAs.
+template <int S, int STEP, int SP, int I0, int I1>
+__device__ __forceinline__ void copy_step(const Ctx& c, bool live, int ts, Frags& C, Frags& N,
+                                          Acc& acc) {
+    copy_tile<SP, I0, I1>(c.src, source_tile(c, ts));
+    load_frags<S>(c.wt, c.wf, c.off[STEP + 1], N);
+    mfma_step(masked(C, live), acc);
+    sched_mix_at<I1 - I0>();
+}
+
 // MASK: the slot may be a padding slot (only in the first pass over the ring).
 template <int S, bool MASK>
 __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
     constexpr int SN = (S + 1) % kFcStages;
     const bool live = !MASK || kt >= c.pad;
-    inner_step<S, 0>(c, live, F0, F1, acc);
+    // Steps 0 .. spread - 2 also issue the rest of the previous slot's
+    // copies, into the stage that slot freed (there is none before slot 0).
+    constexpr bool kTail = !(MASK && S == 0);
+    constexpr int SP = (S + kFcStages - 1) % kFcStages;
+    if constexpr (kTail && kFcSpread >= 2)
+        copy_step<S, 0, SP, copy_begin(1), copy_begin(2)>(c, live, kt - 1 + kFcStages, F0, F1, acc);
+    else
+        inner_step<S, 0>(c, live, F0, F1, acc);
     if constexpr (kFcSteps == 4) {
-        inner_step<S, 1>(c, live, F1, F0, acc);
+        if constexpr (kTail && kFcSpread >= 3)
+            copy_step<S, 1, SP, copy_begin(2), copy_begin(3)>(c, live, kt - 1 + kFcStages, F1, F0, acc);
+        else
+            inner_step<S, 1>(c, live, F1, F0, acc);
         inner_step<S, 2>(c, live, F0, F1, acc);
     }
     wait_copies_and_lds<(kFcStages - 2) * kFcCopies>();  // slots kt + 2 .. may be pending
     ring_barrier();
-    copy_tile<S>(c.src, source_tile(c, kt + kFcStages));
+    copy_tile<S, 0, copy_begin(1)>(c.src, source_tile(c, kt + kFcStages));
     load_frags<SN>(c.wt, c.wf, c.off[0], F0);
     mfma_step(masked(F1, live), acc);
+#if SWIGLU_FC_SPREAD == 0
     sched_copies_reads_among_mfma();
+#else
+    sched_mix_at<copy_begin(1)>();
+#endif
 }
 
 // Slots kt .. kt + stages - 1: one pass over the ring.
