@@ -254,14 +254,15 @@ swiglu_status swiglu_gateup_bias_scale_bwd(const void* dy, int64_t dy_row_stride
  *   y, ldy        [m, n] output, row stride ldy.
  *   x_out, ldx    NULL, or [m, 2n] output receiving A W^T (bf16), stride ldx.
  *   m, n, k       sizes: m >= 0; n a multiple of 64 in [0, 2^30]; k a
- *                 positive multiple of 64 below 2^31 (k may be 0 only when m
- *                 or n is 0).
+ *                 positive multiple of 64 (k may be 0 only when m or n is 0).
  *   dtype         must be SWIGLU_DTYPE_BF16.
- * All pointers must be 16-byte aligned and all row strides multiples of 8.
+ * All pointers must be 16-byte aligned and all row strides multiples of 8;
+ * lda and ldw (hence k) are at most 2^28 elements.
  *
  * Errors: SWIGLU_ERR_BAD_DTYPE (not bf16), SWIGLU_ERR_BAD_SHAPE (n or k not
  * multiples of 64, k == 0 with a non-empty output), SWIGLU_ERR_BAD_STRIDE
- * (strides below the widths, misaligned pointers or strides),
+ * (strides below the widths or lda / ldw above 2^28, misaligned pointers
+ * or strides),
  * SWIGLU_ERR_NULL_POINTER, SWIGLU_ERR_ALIASING (an output overlaps an input
  * or the other output), SWIGLU_ERR_HIP.
  */

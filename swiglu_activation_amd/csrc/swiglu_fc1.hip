@@ -37,6 +37,9 @@
 //  * The copies of a tile are spread thinly over two k steps (one every two
 //    MFMAs), not issued in a burst: a burst fills the copy queue, and the
 //    wave, which issues in order, then stalls in front of its next MFMA.
+//    Each copy is addressed as a wave-uniform base in scalar registers plus
+//    a fixed 32-bit lane offset, so no vector instruction sits between two
+//    copies (which limits lda and ldw to 2^28 elements).
 //  * Rows past m (tokens) or n (features) are clamped to the last valid row:
 //    they copy real data, which reaches only accumulators that are never
 //    stored.
@@ -71,6 +74,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_SCHED
 #define SWIGLU_FC_SCHED 1       // pin the interleaving of MFMAs and memory instructions
 #endif
+#ifndef SWIGLU_FC_SADDR
+#define SWIGLU_FC_SADDR 1       // copies as a wave-uniform base (SGPRs) plus a fixed 32-bit lane offset
+#endif
 #ifndef SWIGLU_FC_SPREAD
 #define SWIGLU_FC_SPREAD 2      // copy issue: 0 packed early in the step after the barrier; N >= 1
 #endif                          // spread evenly over that step and the next N - 1 steps
@@ -102,6 +108,7 @@ constexpr int kFcCopies = kFcRows / kFcCopyRows / kFcWaves;   // copies per thre
 constexpr int kFcMfma = 2 * kFcMF * kFcMT;           // MFMAs per wave per k step
 constexpr int kFcReads = kFcMT + 2 * kFcMF;          // fragment reads per k step
 constexpr int kFcSteps = kFcTileK / 16;              // MFMA k steps per stage
+constexpr int64_t kFcMaxLd = (int64_t)1 << 28;      // largest lda / ldw (elements)
 constexpr int kFcSpread = SWIGLU_FC_SPREAD > 0 ? SWIGLU_FC_SPREAD : 1;   // steps a tile's copies span
 static_assert(kFcSpread <= kFcSteps - 1, "a tile's copies are all issued before the next wait");
 // First copy issued in step j of the span (j = 0: the step after the barrier).
@@ -165,12 +172,48 @@ __device__ __forceinline__ int copy_block(int i, int wave) {
 // fills LDS rows [R q, R q + R) of a stage, R = kFcCopyRows and
 // q = copy_block(i, wave); lane l writes slot l % kFcChunks of row
 // R q + l / kFcChunks, so it reads the chunk that belongs in that slot.
+#if SWIGLU_FC_SADDR
+// Copy i of a wave reads an 8-row block: a wave-uniform base (the block's
+// first row, clamped) and a fixed per-lane byte offset within the block
+// (at most 7 row strides + 112 bytes).
+struct Sources {
+    const char* base[kFcCopies];
+    mutable uint32_t off[kFcCopies];
+};
+#else
 struct Sources {
     const uint16_t* p[kFcCopies];
 };
+#endif
 
 __device__ __forceinline__ void make_sources(const Fc1Args& P, int64_t t0, int64_t f0,
                                              Sources& src) {
+#if SWIGLU_FC_SADDR
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < kFcCopies; ++i) {
+        const int r0 = copy_block(i, wave) * kFcCopyRows;          // the block's first row
+        const int r = r0 + lane / kFcChunks;
+        const int c = chunk_slot(r, lane % kFcChunks);
+        const uint16_t* rowbase;
+        int64_t b, row, ld;
+        if (r0 < kFcRowsA) {
+            rowbase = P.a;
+            ld = P.lda;
+            b = t0 + r0 < P.m ? t0 + r0 : P.m - 1;
+            row = t0 + r < P.m ? t0 + r : P.m - 1;
+        } else {
+            const int w0 = r0 - kFcRowsA, wr = r - kFcRowsA;         // gate rows, then up rows
+            rowbase = P.w + (w0 < kFcTileF ? 0 : P.n) * P.ldw;
+            ld = P.ldw;
+            b = f0 + (w0 % kFcTileF) < P.n ? f0 + (w0 % kFcTileF) : P.n - 1;
+            row = f0 + (wr % kFcTileF) < P.n ? f0 + (wr % kFcTileF) : P.n - 1;
+        }
+        src.base[i] = reinterpret_cast<const char*>(rowbase + b * ld);
+        src.off[i] = (uint32_t)((row - b) * ld * 2 + c * 16);
+    }
+#else
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kFcCopies; ++i) {
@@ -185,11 +228,26 @@ __device__ __forceinline__ void make_sources(const Fc1Args& P, int64_t t0, int64
             src.p[i] = P.w + ((wr < kFcTileF ? 0 : P.n) + f) * P.ldw + c * 8;
         }
     }
+#endif
 }
 
 // Starts copies [I0, I1) of k tile t into stage S.
 template <int S, int I0 = 0, int I1 = kFcCopies>
 __device__ __forceinline__ void copy_tile(const Sources& src, int t) {
+#if SWIGLU_FC_SADDR
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tb = (int64_t)t * kFcTileK * 2;                  // the tile's byte offset
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+        uint16_t* dst = stage<S>() + copy_block(i, wave) * kFcCopyRows * kFcRowElems;
+        // (the offset is made opaque in place, so that the compiler neither
+        // folds base and offset into one loop-invariant vector pointer nor
+        // copies the offset into a scratch register for each copy)
+        asm volatile("" : "+v"(src.off[i]));
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.base[i] + tb + src.off[i]),
+                                         (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
+    }
+#else
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
@@ -198,6 +256,7 @@ __device__ __forceinline__ void copy_tile(const Sources& src, int t) {
             static_cast<const void*>(src.p[i] + (int64_t)t * kFcTileK),
             (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
     }
+#endif
 }
 
 // s_waitcnt: at most N copies (vector memory operations) outstanding, and
@@ -601,6 +660,11 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
     swiglu_status st;
     if ((st = check_operand(m, lda, k, 2)) != SWIGLU_OK) return st;
     if ((st = check_operand(2 * n, ldw, k, 2)) != SWIGLU_OK) return st;
+#if SWIGLU_FC_SADDR
+    // A copy reads 8 rows through one 32-bit byte offset per lane:
+    // 7 row strides + 112 bytes must stay below 2^32.
+    if (lda > kFcMaxLd || ldw > kFcMaxLd) return SWIGLU_ERR_BAD_STRIDE;
+#endif
     if ((st = check_operand(m, ldy, n, 2)) != SWIGLU_OK) return st;
     if (x_out != nullptr && (st = check_operand(m, ldx, 2 * n, 2)) != SWIGLU_OK) return st;
     if (m == 0 || n == 0) return SWIGLU_OK;

@@ -267,6 +267,10 @@ def test_fc1_validation(lib):
     assert call(a=A + 8) == sw.SWIGLU_ERR_BAD_STRIDE
     assert call(y=C + 2) == sw.SWIGLU_ERR_BAD_STRIDE
     assert call(x=D + 4, ldx=256) == sw.SWIGLU_ERR_BAD_STRIDE
+    # the copies address 8 weight or token rows by one 32-bit byte offset:
+    # lda and ldw are at most 2^28 elements
+    assert call(lda=(1 << 28) + 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(ldw=(1 << 28) + 8) == sw.SWIGLU_ERR_BAD_STRIDE
     # NULL inputs or output
     assert call(a=None) == sw.SWIGLU_ERR_NULL_POINTER
     assert call(w=None) == sw.SWIGLU_ERR_NULL_POINTER
