@@ -110,7 +110,11 @@ constexpr int kFcReads = kFcMT + 2 * kFcMF;          // fragment reads per k ste
 constexpr int kFcSteps = kFcTileK / 16;              // MFMA k steps per stage
 constexpr int64_t kFcMaxLd = (int64_t)1 << 28;      // largest lda / ldw (elements)
 constexpr int kFcSpread = SWIGLU_FC_SPREAD > 0 ? SWIGLU_FC_SPREAD : 1;   // steps a tile's copies span
-static_assert(kFcSpread <= kFcSteps - 1, "a tile's copies are all issued before the next wait");
+// The rest of a tile's copies go into the next slot's steps before its last
+// one (steps 0 and 1 of four, step 0 of two); with two stages that slot's
+// wait needs them, so at least one step must follow.
+static_assert(kFcSpread <= (kFcSteps == 4 ? 3 : 2) && (kFcStages > 2 || kFcSpread <= kFcSteps - 1),
+              "a tile's copies are all issued before the wait that needs them");
 // First copy issued in step j of the span (j = 0: the step after the barrier).
 constexpr int copy_begin(int j) { return j * kFcCopies / kFcSpread; }
 static_assert(kFcTileK == 32 || kFcTileK == 64, "4 or 8 chunks per row");
@@ -404,8 +408,10 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t f_tiles, uint32_t t
 // in LDS rows of 72 bf16 (144 bytes, 16-byte aligned rows).
 constexpr int kEpiPitch = kFcWaveF + 8;
 constexpr int kEpiRegion = kFcWaveT * kEpiPitch;
-static_assert(!SWIGLU_FC_LDS_EPI || (kFcWaves == 4 && 2 * kEpiRegion <= kFcStageElems),
-              "two waves' regions per stage, in stages 0 and 1");
+static_assert(!SWIGLU_FC_LDS_EPI ||
+                  (kFcWaves == 4 && (2 * kEpiRegion <= kFcStageElems ||
+                                     (kEpiRegion <= kFcStageElems && kFcStages >= 4))),
+              "the four waves' regions fit two per stage, or one per stage");
 
 // Writes the wave's 128 x 64 tile of one output, value(i, j, e) for
 // accumulator element e of MFMA tile (feature i, token j), to out (row
@@ -597,7 +603,12 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     // output into a private LDS region in registers' order, then reads it
     // back by rows, so each store instruction writes 8 rows of 128 bytes.
     ring_barrier();                                   // every wave is done with the stages
-    uint16_t* region = (wave < 2 ? stage<0>() : stage<1>()) + (wave & 1) * kEpiRegion;
+    uint16_t* region;
+    if constexpr (2 * kEpiRegion <= kFcStageElems)    // two regions per stage (64-wide k)
+        region = (wave < 2 ? stage<0>() : stage<1>()) + (wave & 1) * kEpiRegion;
+    else                                              // one per stage (32-wide k, 4+ stages)
+        region = wave == 0 ? stage<0>() : wave == 1 ? stage<1>() : wave == 2 ? stage<2 % kFcStages>()
+                                                                             : stage<3 % kFcStages>();
     const int64_t tw = t0 + c.wt, fw = f0 + c.wf;     // the wave's first token and feature
     epi_out(region, tw, fw, P.m, P.n, P.y, P.ldy, [&](int i, int j, int e) {
         const float g = acc.g[i][j][e];
