@@ -81,9 +81,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define SWIGLU_FC_SPREAD 2      // copy issue: 0 packed early in the step after the barrier; N >= 1
 #endif                          // spread evenly over that step and the next N - 1 steps
 
-constexpr int kFcWaveT = 128;                        // tokens per wave
+#ifndef SWIGLU_FC_WAVES
+#define SWIGLU_FC_WAVES 4       // waves per workgroup: 4 (128 x 64 wave tiles) or 8 (64 x 64)
+#endif
+static_assert(SWIGLU_FC_WAVES == 4 || SWIGLU_FC_WAVES == 8, "wave count");
+constexpr int kFcWaveT = SWIGLU_FC_WAVES == 4 ? 128 : 64;   // tokens per wave
 constexpr int kFcWaveF = 64;                         // features per wave (gate and up each)
-constexpr int kFcWavesT = 2, kFcWavesF = 2;
+constexpr int kFcWavesT = SWIGLU_FC_WAVES / 2, kFcWavesF = 2;
 constexpr int kFcWaves = kFcWavesT * kFcWavesF;
 constexpr int kFcThreads = 64 * kFcWaves;
 constexpr int kFcMT = kFcWaveT / 32;                 // 32x32 tiles per wave along tokens
@@ -152,6 +156,16 @@ __device__ __forceinline__ uint16_t* stage() {
 #if SWIGLU_FC_STAGES == 5
     else return fc_stage4;
 #endif
+}
+
+// Stage s, chosen at run time (0 <= s < stages).
+__device__ __forceinline__ uint16_t* stage_at(int s) {
+    uint16_t* p = stage<0>();
+    if (s == 1) p = stage<1>();
+    if constexpr (kFcStages > 2) if (s == 2) p = stage<2 % kFcStages>();
+    if constexpr (kFcStages > 3) if (s == 3) p = stage<3 % kFcStages>();
+    if constexpr (kFcStages > 4) if (s == 4) p = stage<4 % kFcStages>();
+    return p;
 }
 
 // Slot of 16-byte chunk c in LDS row r. A fragment read takes one chunk
@@ -353,10 +367,11 @@ __device__ __forceinline__ void sched_reads_among_mfma() {
 #endif
 }
 
+template <int kUnused = 0>
 __device__ __forceinline__ void sched_copies_reads_among_mfma() {
 #if SWIGLU_FC_SCHED
     constexpr int per = kFcCopies / kFcReads;        // copies per fragment read
-    static_assert(per * kFcReads == kFcCopies, "copies spread evenly over the reads");
+    static_assert(kUnused != 0 || per * kFcReads == kFcCopies, "copies spread evenly over the reads");
 #pragma unroll
     for (int q = 0; q < kFcReads; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSgVmemRead, per, 0);
@@ -404,16 +419,19 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t f_tiles, uint32_t t
     ft = in / gs;
 }
 
-// Epilogue staging: a wave's tile (128 tokens x 64 features of one output)
+// Epilogue staging: a wave's tile (kFcWaveT tokens x 64 features of one output)
 // in LDS rows of 72 bf16 (144 bytes, 16-byte aligned rows).
 constexpr int kEpiPitch = kFcWaveF + 8;
 constexpr int kEpiRegion = kFcWaveT * kEpiPitch;
+// Regions per stage (at most half the waves, so that they spread over two
+// or more stages) and the stages they take.
+constexpr int kEpiPerStage = kFcStageElems / kEpiRegion < kFcWaves / 2 ? kFcStageElems / kEpiRegion
+                                                                         : kFcWaves / 2;
 static_assert(!SWIGLU_FC_LDS_EPI ||
-                  (kFcWaves == 4 && (2 * kEpiRegion <= kFcStageElems ||
-                                     (kEpiRegion <= kFcStageElems && kFcStages >= 4))),
-              "the four waves' regions fit two per stage, or one per stage");
+                  (kEpiPerStage >= 1 && (kFcWaves + kEpiPerStage - 1) / kEpiPerStage <= kFcStages),
+              "every wave's region fits in the stages");
 
-// Writes the wave's 128 x 64 tile of one output, value(i, j, e) for
+// Writes the wave's kFcWaveT x 64 tile of one output, value(i, j, e) for
 // accumulator element e of MFMA tile (feature i, token j), to out (row
 // stride ld) at token tw, feature fw, skipping tokens >= m and features >= n.
 // Register e of a 32x32 tile holds feature (e % 4) + 8 (e / 4) + 4 (lane / 32)
@@ -603,12 +621,7 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     // output into a private LDS region in registers' order, then reads it
     // back by rows, so each store instruction writes 8 rows of 128 bytes.
     ring_barrier();                                   // every wave is done with the stages
-    uint16_t* region;
-    if constexpr (2 * kEpiRegion <= kFcStageElems)    // two regions per stage (64-wide k)
-        region = (wave < 2 ? stage<0>() : stage<1>()) + (wave & 1) * kEpiRegion;
-    else                                              // one per stage (32-wide k, 4+ stages)
-        region = wave == 0 ? stage<0>() : wave == 1 ? stage<1>() : wave == 2 ? stage<2 % kFcStages>()
-                                                                             : stage<3 % kFcStages>();
+    uint16_t* region = stage_at(wave / kEpiPerStage) + (wave % kEpiPerStage) * kEpiRegion;
     const int64_t tw = t0 + c.wt, fw = f0 + c.wf;     // the wave's first token and feature
     epi_out(region, tw, fw, P.m, P.n, P.y, P.ldy, [&](int i, int j, int e) {
         const float g = acc.g[i][j][e];
