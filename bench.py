@@ -162,6 +162,34 @@ def cpu_baseline_other_rows(w, x_h, dy_h, rows: int = 512):
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 
 
+def pair_times(stream, f1, f2, iters: int, warm: int = 2):
+    """Mean event times (ms) of f1 and of f2, run alternately iters + warm
+    times back to back on `stream`, the first `warm` pairs discarded. One
+    synchronisation at the end, so the GPU never idles between launches."""
+    import numpy as np
+    import torch
+    ev = []
+    for _ in range(iters + warm):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        f1()
+        b.record(stream)
+        f2()
+        c.record(stream)
+        ev.append((a, b, c))
+    ev[-1][2].synchronize()
+    t = [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev[warm:]]
+    return float(np.mean([x[0] for x in t])), float(np.mean([x[1] for x in t]))
+
+
+def hbm_roofline(kernel: str, bytes_: float, ms: float) -> dict:
+    """Roofline object of an HBM-bound kernel: algorithmic bytes over its
+    average event-timed launch, against the 8 TB/s peak."""
+    achieved = bytes_ / ms / 1e6
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "bytes_per_launch": bytes_}
+
+
 def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iters: int = 10,
             clock_warmup_s: float = 0.3):
     """fc1 projection with the SwiGLU epilogue (one kernel) against
@@ -227,7 +255,6 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
 def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
     """Bias + per-token scale variants on the workload's tensors: forward,
     and backward with dx, dbias and dscale (the reductions included)."""
-    import numpy as np
     import torch
 
     import swiglu_activation_amd as sw
@@ -239,37 +266,30 @@ def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
     scale_t = torch.rand(w.shape[:-1], device=dev, generator=gen) * 0.95 + 0.05
     ws = torch.empty(sw.swiglu_gateup_bias_scale_workspace_size(w.rows, w.n, True, True),
                      dtype=torch.uint8, device=dev)
-    bt = []
-    for k in range(iters + 2):
-        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record(stream)
-        sw.swiglu_gateup_bias_scale_fwd(x, bias_t, scale_t, y)
-        b.record(stream)
-        sw.swiglu_gateup_bias_scale_bwd(dy, x, bias_t, scale_t, dx, workspace=ws)
-        c.record(stream)
-        c.synchronize()
-        if k >= 2:
-            bt.append((a.elapsed_time(b), b.elapsed_time(c)))
-    bf, bb = float(np.mean([t[0] for t in bt])), float(np.mean([t[1] for t in bt]))
+    bf, bb = pair_times(stream, lambda: sw.swiglu_gateup_bias_scale_fwd(x, bias_t, scale_t, y),
+                        lambda: sw.swiglu_gateup_bias_scale_bwd(dy, x, bias_t, scale_t, dx,
+                                                                workspace=ws), iters)
     # the routed-expert form: a per-token scale and no bias, dx and dscale
-    st = []
-    for k in range(iters + 2):
-        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record(stream)
-        sw.swiglu_gateup_bias_scale_fwd(x, None, scale_t, y)
-        b.record(stream)
-        sw.swiglu_gateup_bias_scale_bwd(dy, x, None, scale_t, dx, workspace=ws)
-        c.record(stream)
-        c.synchronize()
-        if k >= 2:
-            st.append((a.elapsed_time(b), b.elapsed_time(c)))
-    sf, sb = float(np.mean([t[0] for t in st])), float(np.mean([t[1] for t in st]))
+    sf, sb = pair_times(stream, lambda: sw.swiglu_gateup_bias_scale_fwd(x, None, scale_t, y),
+                        lambda: sw.swiglu_gateup_bias_scale_bwd(dy, x, None, scale_t, dx,
+                                                                workspace=ws), iters)
+    # algorithmic bytes: the base op's, plus one read of the bias row and the
+    # scales, plus the fp32 dbias and dscale written by the backward
+    extra_in = 2 * w.n * e + 4 * w.rows
+    fwd_alg, bwd_alg = fwd_bytes + extra_in, bwd_bytes + extra_in + 4 * 2 * w.n + 4 * w.rows
     return {"fwd_ms": round(bf, 5), "bwd_ms": round(bb, 5),
+            "roofline_fwd": hbm_roofline("swiglu_fwd_bs_kernel (bias, scale)", fwd_alg, bf),
+            "roofline_bwd": hbm_roofline("swiglu_bwd_bs_kernel + sums (dx, dbias, dscale)",
+                                         bwd_alg, bb),
             "fwd_GBps": round(fwd_bytes / bf / 1e6, 1),
             "bwd_GBps": round(bwd_bytes / bb / 1e6, 1),
             "what": "z = x + bias, y = s * silu(z_g) * z_u; bwd writes dx, dbias, "
                     "dscale (GB/s on the base op's bytes)",
             "scale_only": {"fwd_ms": round(sf, 5), "bwd_ms": round(sb, 5),
+                           "roofline_fwd": hbm_roofline("swiglu_fwd_bs_kernel (scale)",
+                                                        fwd_bytes + 4 * w.rows, sf),
+                           "roofline_bwd": hbm_roofline("swiglu_bwd_bs1_kernel + sum (dx, dscale)",
+                                                        bwd_bytes + 8 * w.rows, sb),
                            "fwd_GBps": round(fwd_bytes / sf / 1e6, 1),
                            "bwd_GBps": round(bwd_bytes / sb / 1e6, 1),
                            "what": "no bias, per-token scale; bwd writes dx and dscale"}}
@@ -519,19 +539,11 @@ def main():
         dy2 = dy.reshape(w.rows, w.n)
         y2 = y.reshape(w.rows, w.n)
         dg2, du2 = dx.reshape(w.rows, 2 * w.n)[:, :w.n], dx.reshape(w.rows, 2 * w.n)[:, w.n:]
-        tt = []
-        for k in range(12):
-            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            a.record(stream)
-            sw.swiglu_silu_mul_fwd(gate, upv, y2)
-            b.record(stream)
-            sw.swiglu_silu_mul_bwd(dy2, gate, upv, dg2, du2)
-            c.record(stream)
-            c.synchronize()
-            if k >= 2:
-                tt.append((a.elapsed_time(b), b.elapsed_time(c)))
-        tf, tb = float(np.mean([t[0] for t in tt])), float(np.mean([t[1] for t in tt]))
+        tf, tb = pair_times(stream, lambda: sw.swiglu_silu_mul_fwd(gate, upv, y2),
+                            lambda: sw.swiglu_silu_mul_bwd(dy2, gate, upv, dg2, du2), 10)
         passes["two_tensor_views"] = {"fwd_ms": round(tf, 5), "bwd_ms": round(tb, 5),
+                                      "roofline_fwd": hbm_roofline("swiglu_silu_mul fwd", fwd_bytes, tf),
+                                      "roofline_bwd": hbm_roofline("swiglu_silu_mul bwd", bwd_bytes, tb),
                                       "fwd_GBps": round(fwd_bytes / tf / 1e6, 1),
                                       "bwd_GBps": round(bwd_bytes / tb / 1e6, 1)}
         log(f"[bench] autograd step {ag_ms:.4f} ms; two-tensor fwd {tf:.4f} ms bwd {tb:.4f} ms")
