@@ -131,6 +131,7 @@ def cpu_baseline_other_rows(w, x_h, dy_h, rows: int = 512):
 
     import oracle
     out = {}
+    rows = min(rows, w.rows)
     rng = np.random.default_rng(w.seed)
     with threadpool_limits(limits=1):
         # bias + scale: forward and backward (dx, dbias, dscale) on `rows` rows

@@ -1,0 +1,73 @@
+"""bench.py's host-side contract, on the CPU: the one-GPU refusal, the exit
+without a GPU, the roofline object and the oracle timing legs."""
+import os
+import subprocess
+import sys
+import types
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300, cwd=ROOT)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = _run("--gpus", "2", "--steps", "3", "--warmup", "1")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the exit without a GPU")
+def test_exits_without_a_gpu():
+    r = _run("--steps", "1", "--warmup", "0")
+    assert r.returncode == 1
+    assert "needs a GPU" in r.stderr and r.stdout == ""
+
+
+def test_hbm_roofline_object():
+    r = bench.hbm_roofline("k", 4.0e9, 0.5)          # 4 GB in 0.5 ms = 8000 GB/s
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.PEAK_GBPS
+    assert r["achieved"] == pytest.approx(8000.0) and r["frac"] == pytest.approx(1.0)
+    assert r["bytes_per_launch"] == 4.0e9
+
+
+def _small_workload(rows=64, n=256):
+    rng = np.random.default_rng(0)
+    # bf16 bit patterns of modest normal values: sign, exponents 120..130
+    def bits(shape):
+        e = rng.integers(120, 131, size=shape).astype(np.uint16)
+        return ((rng.integers(0, 2, size=shape).astype(np.uint16) << 15) | (e << 7)
+                | rng.integers(0, 128, size=shape).astype(np.uint16))
+    w = types.SimpleNamespace(rows=rows, n=n, dtype="bf16", elem_bytes=2, name="small", seed=0)
+    return w, bits((rows, 2 * n)), bits((rows, n))
+
+
+def test_cpu_baseline_covers_the_sample_it_reports():
+    # fewer rows than the 512 the bias / scale sample takes by default
+    w, x, dy = _small_workload(rows=256, n=2048)
+    r = bench.cpu_baseline(w, x, dy, seconds=30.0)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s"
+    assert r["sample"].startswith(f"rows 0..{w.rows} of {w.rows}")
+    assert r["value"] > 0 and r["seconds"] > 0
+    # (seconds is reported to the millisecond)
+    assert r["value"] == pytest.approx(8 * 2 * w.rows * w.n / r["seconds"] / 1e9, rel=0.05)
+    a = r["all_cores"]
+    assert 1 <= a["cores"] <= 16 and a["value"] > 0
+    assert set(r["other_rows"]) == {"bias_scale", "fc1_swiglu"}
+
+
+def test_all_cores_leg_runs_every_block():
+    # a row count that is not a multiple of the block: the last block is short
+    w, x, dy = _small_workload(rows=70)
+    r = bench.cpu_baseline_all_cores(w, x, dy, block=32, max_threads=4)
+    assert r["cores"] == min(4, len(os.sched_getaffinity(0)))
+    assert f"all {w.rows} rows" in r["sample"]
