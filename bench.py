@@ -66,27 +66,56 @@ def read_traffic():
     return float(t.group(1))
 
 
-def cpu_baseline(w, x_h, dy_h, seconds: float):
+def cpu_baseline(w, x_h, dy_h, seconds: float, outputs=None):
     """The oracle as it stands, in one process, on a bounded sample of the
     workload: consecutive 512-row blocks from row 0 until about `seconds` of
-    CPU time is spent (or the rows run out)."""
+    CPU time is spent in it (or the rows run out).
+
+    outputs: optionally the GPU's y and dx of the timed step, as stored
+    ([rows, n] and [rows, 2n]; bf16 as bit patterns). The oracle's values of
+    the sampled rows are then also compared with them, outside the timed
+    part: bf16 by ulp distance to the correctly rounded value, fp32 by
+    relative error."""
+    import numpy as np
+
     import oracle
     rows = 0
-    t0 = time.perf_counter()
-    while rows < w.rows and time.perf_counter() - t0 < seconds:
+    dt = 0.0
+    worst = {"fwd": 0.0, "bwd": 0.0}
+    over = 0
+    while rows < w.rows and dt < seconds:
         r1 = min(rows + 512, w.rows)
+        t0 = time.perf_counter()
         xf = oracle.widen(x_h[rows:r1], w.dtype)
         dyf = oracle.widen(dy_h[rows:r1], w.dtype)
         y = oracle.oracle_fwd(xf)
         dx = oracle.oracle_bwd(xf, dyf)
+        dt += time.perf_counter() - t0
         assert y.shape == (r1 - rows, w.n) and dx.shape == (r1 - rows, 2 * w.n)
+        if outputs is not None:
+            for what, got, ref in (("fwd", outputs[0][rows:r1], y), ("bwd", outputs[1][rows:r1], dx)):
+                if w.dtype == "bf16":
+                    d = oracle.bf16_ulp_distance(got, oracle.round_f64_to_bf16_bits(ref))
+                    over += int(np.count_nonzero(d > 2))
+                else:
+                    g = np.asarray(got, dtype=np.float64)
+                    d = np.abs(g - ref) / np.maximum(np.abs(ref), np.finfo(np.float32).tiny)
+                worst[what] = max(worst[what], float(d.max()))
         rows = r1
-    dt = time.perf_counter() - t0
     bytes_ = 8 * w.elem_bytes * rows * w.n
+    parity = None
+    if outputs is not None:
+        if w.dtype == "bf16":
+            parity = {"rows": rows, "elements": 3 * rows * w.n, "max_ulp_fwd": int(worst["fwd"]),
+                      "max_ulp_bwd": int(worst["bwd"]), "over_2_ulp": over}
+        else:
+            parity = {"rows": rows, "elements": 3 * rows * w.n, "max_rel_fwd": worst["fwd"],
+                      "max_rel_bwd": worst["bwd"]}
     return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"rows 0..{rows} of {w.rows} ({rows * w.n} gate/up pairs) of {w.name}: "
                       "widen to float64, forward, backward (numpy, one thread)",
+            "timed_outputs_vs_oracle": parity,
             "all_cores": cpu_baseline_all_cores(w, x_h, dy_h),
             "other_rows": cpu_baseline_other_rows(w, x_h, dy_h)}
 
@@ -467,6 +496,17 @@ def main():
     log(f"[bench] step {ms_per_step:.4f} ms -> {value:.1f} GB/s; fwd {fwd_avg:.4f} ms, "
         f"bwd {bwd_avg:.4f} ms")
 
+    # The outputs of the timed step, kept for the oracle comparison in the
+    # CPU-baseline leg (later legs overwrite y and dx).
+    timed_outputs = None
+    if not args.no_cpu_baseline:
+        def stored(t, cols):
+            a = t.reshape(w.rows, cols)
+            if w.dtype == "bf16":
+                return a.view(torch.int16).cpu().numpy().view(np.uint16)
+            return a.cpu().numpy()
+        timed_outputs = (stored(y, w.n), stored(dx, 2 * w.n))
+
     passes = {
         "fwd": {"ms_avg": round(fwd_avg, 5), "ms_min": round(min(fwd_ms), 5),
                 "GBps": round(fwd_bytes / fwd_avg / 1e6, 1), "bytes": fwd_bytes},
@@ -622,7 +662,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for about {args.cpu_seconds} s")
-        out["cpu_baseline"] = cpu_baseline(w, x_h, dy_h, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, x_h, dy_h, args.cpu_seconds, timed_outputs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

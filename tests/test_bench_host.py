@@ -71,3 +71,23 @@ def test_all_cores_leg_runs_every_block():
     r = bench.cpu_baseline_all_cores(w, x, dy, block=32, max_threads=4)
     assert r["cores"] == min(4, len(os.sched_getaffinity(0)))
     assert f"all {w.rows} rows" in r["sample"]
+
+
+def test_cpu_baseline_compares_the_timed_outputs_with_the_oracle():
+    import oracle
+    w, x, dy = _small_workload(rows=48, n=128)
+    xf, dyf = oracle.widen(x, "bf16"), oracle.widen(dy, "bf16")
+    y = oracle.round_f64_to_bf16_bits(oracle.oracle_fwd(xf))
+    dx = oracle.round_f64_to_bf16_bits(oracle.oracle_bwd(xf, dyf))
+    r = bench.cpu_baseline(w, x, dy, seconds=30.0, outputs=(y, dx))["timed_outputs_vs_oracle"]
+    assert r == {"rows": 48, "elements": 3 * 48 * 128, "max_ulp_fwd": 0, "max_ulp_bwd": 0,
+                 "over_2_ulp": 0}
+    # a planted error of 3 ulp in one dgate element (away from zero and the
+    # binade edges) is reported
+    dx_bad = dx.copy()
+    i, j = 17, 5
+    dx_bad[i, j] = np.uint16(int(dx_bad[i, j]) + (3 if (dx_bad[i, j] & 0x7F) < 0x7C else -3))
+    r = bench.cpu_baseline(w, x, dy, seconds=30.0, outputs=(y, dx_bad))["timed_outputs_vs_oracle"]
+    assert r["max_ulp_fwd"] == 0 and r["max_ulp_bwd"] == 3 and r["over_2_ulp"] == 1
+    # without outputs there is no comparison
+    assert bench.cpu_baseline(w, x, dy, seconds=30.0)["timed_outputs_vs_oracle"] is None
