@@ -64,11 +64,58 @@ __device__ __forceinline__ void widen_bits(typename Vec<T, VEC>::R r, float (&f)
     }
 }
 
+#ifndef SWIGLU_BS_FWD_ROWS
+#define SWIGLU_BS_FWD_ROWS 2    // rows per lane in the wide forward with a bias (1 or 2)
+#endif
+constexpr int kFwdBiasRows = SWIGLU_BS_FWD_ROWS;
+static_assert(kFwdBiasRows == 1 || kFwdBiasRows == 2, "rows per lane");
+
 template <typename T, int VEC, bool WIDE, bool HAS_BIAS, bool HAS_SCALE>
 __global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
     const T* __restrict__ gp, int64_t gs, const T* __restrict__ up, int64_t us,
     T* __restrict__ y, int64_t ys, const T* __restrict__ bg, const T* __restrict__ bu,
     const float* __restrict__ sc, int64_t scs, Geom G) {
+    if constexpr (WIDE && HAS_BIAS && kFwdBiasRows == 2) {
+        // Block (x, y) takes vectors [256 x, 256 x + 256) of rows 2y and
+        // 2y + 1; each lane loads its bias vectors once for both rows.
+        const uint32_t col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+        if (col >= G.nv) return;
+        const int64_t r0 = 2 * (int64_t)blockIdx.y;
+        const bool two = r0 + 1 < G.rows;                  // uniform
+        const int64_t c = (int64_t)col * VEC;
+        typedef typename Vec<T, VEC>::R R;
+        const R g0 = load_raw<R>(gp + r0 * gs + c);
+        const R u0 = load_raw<R>(up + r0 * us + c);
+        R g1{}, u1{};
+        if (two) {
+            g1 = load_raw<R>(gp + (r0 + 1) * gs + c);
+            u1 = load_raw<R>(up + (r0 + 1) * us + c);
+        }
+        const R bgr = *reinterpret_cast<const R*>(bg + c);
+        const R bur = *reinterpret_cast<const R*>(bu + c);
+        const float s0 = HAS_SCALE ? sc[r0 * scs] : 1.0f;
+        const float s1 = HAS_SCALE && two ? sc[(r0 + 1) * scs] : 1.0f;
+        float b[VEC], d[VEC];
+        widen_bits<T, VEC>(bgr, b);
+        widen_bits<T, VEC>(bur, d);
+        auto one_row = [&](const R& gr, const R& ur, float s, T* dst) {
+            float g[VEC], u[VEC], out[VEC];
+            widen_bits<T, VEC>(gr, g);
+            widen_bits<T, VEC>(ur, u);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                g[i] += b[i];
+                u[i] += d[i];
+                float sig, osig;
+                sigmoid_pair<T, false>(g[i], sig, osig);
+                out[i] = HAS_SCALE ? ((g[i] * sig) * u[i]) * s : (g[i] * sig) * u[i];
+            }
+            Vec<T, VEC>::store(dst, out);
+        };
+        one_row(g0, u0, s0, y + r0 * ys + c);
+        if (two) one_row(g1, u1, s1, y + (r0 + 1) * ys + c);
+        return;
+    }
     int64_t row;
     uint32_t col;
     if (!locate<WIDE>(G, row, col)) return;
@@ -410,7 +457,8 @@ swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
         y = const_cast<T*>(static_cast<const T*>(ops[2].p)) + r0 * ys;
         sc = A.scale != nullptr ? A.scale + r0 * scs : nullptr;
         G.rows = rc;
-        const dim3 grid = P.wide ? dim3(P.tiles, (uint32_t)rc)
+        const uint32_t gy = (uint32_t)(hb && kFwdBiasRows == 2 ? (rc + 1) / 2 : rc);
+        const dim3 grid = P.wide ? dim3(P.tiles, gy)
                                  : dim3(swiglu_host::flat_blocks(rc, P.nv, kBlock), 1);
         if (hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream) != hipSuccess)
             return SWIGLU_ERR_HIP;
