@@ -97,6 +97,20 @@ inline uint32_t flat_blocks(int64_t rows, uint32_t nv, uint32_t block) {
     return (uint32_t)((rows * nv + block - 1) / block);
 }
 
+// fc1 launches: token rows per launch when n features are cut in tiles of
+// tile_f and tokens in tiles of tile_t, on a 1D grid of f_tiles x t_tiles
+// workgroups of `threads` work-items. The grid's work-item count stays below
+// 2^32 and a launch takes at most max_t token tiles. 0 when not even one
+// token tile fits (the caller rejects that n).
+inline int64_t fc1_rows_per_launch(int64_t n, int64_t tile_f, int64_t tile_t, int64_t max_t,
+                                   int64_t threads) {
+    const int64_t f_tiles = (n + tile_f - 1) / tile_f;
+    const int64_t max_wg = (((int64_t)1 << 32) - 1) / threads;
+    int64_t t = f_tiles > 0 ? max_wg / f_tiles : max_t;
+    if (t > max_t) t = max_t;
+    return t * tile_t;
+}
+
 }  // namespace swiglu_host
 
 #endif  // SWIGLU_HOST_LOGIC_H

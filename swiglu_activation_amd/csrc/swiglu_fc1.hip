@@ -722,12 +722,10 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
     P.n = n;
     P.k = k;
     const uint32_t f_tiles = (uint32_t)((n + kFcTileF - 1) / kFcTileF);
-    // One launch covers at most 2^24 - 1 workgroups (its work-item count must
-    // stay below 2^32) and 65535 token tiles.
-    const int64_t max_wg = ((int64_t)1 << 24) - 1;
-    int64_t tiles_per_launch = max_wg / f_tiles;
-    if (tiles_per_launch > kMaxGridY) tiles_per_launch = kMaxGridY;
-    const int64_t rows_per_launch = tiles_per_launch * kFcTileT;
+    // One launch stays below 2^32 work-items and takes at most 65535 token tiles.
+    const int64_t rows_per_launch =
+        swiglu_host::fc1_rows_per_launch(n, kFcTileF, kFcTileT, kMaxGridY, kFcThreads);
+    if (rows_per_launch <= 0) return SWIGLU_ERR_BAD_SHAPE;
     uint32_t t_tiles = 0;
     void* args[] = {&P, const_cast<uint32_t*>(&f_tiles), &t_tiles};
     for (int64_t r0 = 0; r0 < m; r0 += rows_per_launch) {

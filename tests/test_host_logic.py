@@ -45,6 +45,10 @@ int main() {
             long long rows; unsigned nv, block;
             std::scanf("%lld %u %u", &rows, &nv, &block);
             std::printf("%u\n", flat_blocks(rows, nv, block));
+        } else if (op == 'F') {
+            long long n, tf, tt, maxt, threads;
+            std::scanf("%lld %lld %lld %lld %lld", &n, &tf, &tt, &maxt, &threads);
+            std::printf("%lld\n", (long long)fc1_rows_per_launch(n, tf, tt, maxt, threads));
         }
     }
     return 0;
@@ -158,3 +162,28 @@ def test_flat_lane_to_row_division_is_exact():
         L = L[(L >= 0) & (L <= top)].astype(np.uint64)
         q = np.floor((L.astype(np.float64) + 0.5) * inv).astype(np.uint64)
         assert np.array_equal(q, L // nv), nv
+
+
+@pytest.mark.parametrize("threads", [256, 512])
+def test_fc1_launch_chunks(driver, threads):
+    """fc1's token rows per launch: the largest whole number of 256-token
+    tiles (at most 65535) whose grid of f_tiles x t_tiles workgroups stays
+    below 2^32 work-items, for n across its whole range; 0 only where not
+    one tile fits."""
+    ns = sorted({64, 128, 192, 4096, 32768, 1 << 20, (1 << 23) + 64, (1 << 24) - 64,
+                 (1 << 29) + 128, (1 << 30) - 128, 1 << 30}
+                | {int(v) * 64 for v in np.random.default_rng(5).integers(1, 1 << 24, 40)})
+    got = driver([f"F {n} 128 256 65535 {threads}" for n in ns])
+    for n, line in zip(ns, got):
+        rpl = int(line)
+        f_tiles = -(-n // 128)
+        fits = lambda t: f_tiles * t * threads < (1 << 32) and t <= 65535
+        assert rpl % 256 == 0
+        t = rpl // 256
+        if t == 0:
+            assert not fits(1), n
+        else:
+            assert fits(t) and not fits(t + 1), (n, t)
+    # at the default 256 threads every n up to 2^30 gets at least one tile
+    if threads == 256:
+        assert all(int(line) > 0 for line in got)
