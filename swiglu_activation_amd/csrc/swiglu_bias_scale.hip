@@ -26,7 +26,7 @@ using namespace swiglu_impl;
 #define SWIGLU_BS_ROWS_PER_GROUP 128   // rows reduced in registers per block (backward)
 #endif
 #ifndef SWIGLU_BS_PREFETCH
-#define SWIGLU_BS_PREFETCH 1           // load the next row while computing this one (backward)
+#define SWIGLU_BS_PREFETCH 2           // rows loaded ahead of the one computed (backward): 0, 1 or 2
 #endif
 #ifndef SWIGLU_BS_ONE_SHOT
 #define SWIGLU_BS_ONE_SHOT 1           // backward without dbias on wide rows: one-shot grid
@@ -267,7 +267,39 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs_kernel(
                 part_ds[((int64_t)blockIdx.x * kWaves + wave) * G.total_rows + G.row0 + row] = w;
         }
     };
-#if SWIGLU_BS_PREFETCH
+#if SWIGLU_BS_PREFETCH == 2
+    // Rows j + 1 and j + 2 are loaded (as raw bits) while row j is computed.
+    typedef typename Vec<T, VEC>::R R;
+    R g0{}, u0{}, d0{}, g1{}, u1{}, d1{};
+    float s0 = 1.0f, s1 = 1.0f;
+    auto load_row2 = [&](int j, R& gg, R& uu, R& dd, float& ss) {
+        const int64_t rr = r_first + j * r_step;
+        if (j < kBsRows && rr < G.rows) {             // uniform
+            if (active) {
+                gg = load_raw<R>(gp + rr * gs + c);
+                uu = load_raw<R>(up + rr * us + c);
+                dd = load_raw<R>(dyp + rr * dys + c);
+            }
+            if (sc != nullptr) ss = sc[rr * scs];
+        }
+    };
+    load_row2(0, g0, u0, d0, s0);
+    load_row2(1, g1, u1, d1, s1);
+    for (int j = 0; j < kBsRows; ++j) {
+        const int64_t row = r_first + j * r_step;
+        if (row >= G.rows) break;                     // uniform
+        R g2{}, u2{}, d2{};
+        float s2 = 1.0f;
+        load_row2(j + 2, g2, u2, d2, s2);
+        float g[VEC], u[VEC], d[VEC];
+        widen_bits<T, VEC>(g0, g);
+        widen_bits<T, VEC>(u0, u);
+        widen_bits<T, VEC>(d0, d);
+        row_step(row, s0, g, u, d);
+        g0 = g1; u0 = u1; d0 = d1; s0 = s1;
+        g1 = g2; u1 = u2; d1 = d2; s1 = s2;
+    }
+#elif SWIGLU_BS_PREFETCH
     // Row j + 1 is loaded (as raw bits) while row j is computed, so two rows
     // of loads are in flight per wave.
     typedef typename Vec<T, VEC>::R R;
