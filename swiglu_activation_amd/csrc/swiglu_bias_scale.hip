@@ -64,18 +64,18 @@ __device__ __forceinline__ void widen_bits(typename Vec<T, VEC>::R r, float (&f)
     }
 }
 
-#ifndef SWIGLU_BS_FWD_ROWS
-#define SWIGLU_BS_FWD_ROWS 2    // rows per lane in the wide forward with a bias (1 or 2)
+#ifndef SWIGLU_BS_BIAS_ROWS
+#define SWIGLU_BS_BIAS_ROWS 2    // rows per lane with a bias: wide forward, one-shot backward (1 or 2)
 #endif
-constexpr int kFwdBiasRows = SWIGLU_BS_FWD_ROWS;
-static_assert(kFwdBiasRows == 1 || kFwdBiasRows == 2, "rows per lane");
+constexpr int kBiasRows = SWIGLU_BS_BIAS_ROWS;
+static_assert(kBiasRows == 1 || kBiasRows == 2, "rows per lane");
 
 template <typename T, int VEC, bool WIDE, bool HAS_BIAS, bool HAS_SCALE>
 __global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
     const T* __restrict__ gp, int64_t gs, const T* __restrict__ up, int64_t us,
     T* __restrict__ y, int64_t ys, const T* __restrict__ bg, const T* __restrict__ bu,
     const float* __restrict__ sc, int64_t scs, Geom G) {
-    if constexpr (WIDE && HAS_BIAS && kFwdBiasRows == 2) {
+    if constexpr (WIDE && HAS_BIAS && kBiasRows == 2) {
         // Block (x, y) takes vectors [256 x, 256 x + 256) of rows 2y and
         // 2y + 1; each lane loads its bias vectors once for both rows.
         const uint32_t col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
@@ -377,6 +377,58 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs1_kernel(
         dup = up;
         dus = us;
     }
+    if constexpr (HAS_BIAS && kBiasRows == 2) {
+        // As in the forward: block (x, y) takes rows 2y and 2y + 1, and each
+        // lane loads its bias vectors once for both.
+        const int64_t r0 = 2 * (int64_t)blockIdx.y;
+        const bool two = r0 + 1 < G.rows;                  // uniform
+        const uint32_t col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+        const bool active = col < G.nv;
+        if (!WANT_DS && !active) return;
+        const int64_t c = (int64_t)col * VEC;
+        typedef typename Vec<T, VEC>::R R;
+        R g0{}, u0{}, d0{}, g1{}, u1{}, d1{}, bgr{}, bur{};
+        if (active) {
+            g0 = load_raw<R>(gp + r0 * gs + c);
+            u0 = load_raw<R>(up + r0 * us + c);
+            d0 = load_raw<R>(dyp + r0 * dys + c);
+            if (two) {
+                g1 = load_raw<R>(gp + (r0 + 1) * gs + c);
+                u1 = load_raw<R>(up + (r0 + 1) * us + c);
+                d1 = load_raw<R>(dyp + (r0 + 1) * dys + c);
+            }
+            bgr = *reinterpret_cast<const R*>(bg + c);
+            bur = *reinterpret_cast<const R*>(bu + c);
+        }
+        const float s0 = HAS_SCALE ? sc[r0 * scs] : 1.0f;
+        const float s1 = HAS_SCALE && two ? sc[(r0 + 1) * scs] : 1.0f;
+        float b[VEC], e[VEC];
+        widen_bits<T, VEC>(bgr, b);
+        widen_bits<T, VEC>(bur, e);
+        auto one_row = [&](int64_t row, const R& gr, const R& ur, const R& dr, float s) {
+            float p = 0.0f;
+            if (active) {
+                float g[VEC], u[VEC], d[VEC], dg[VEC], du[VEC];
+                widen_bits<T, VEC>(gr, g);
+                widen_bits<T, VEC>(ur, u);
+                widen_bits<T, VEC>(dr, d);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i)
+                    bwd_bs_elem<T>(g[i], u[i], d[i], b[i], e[i], s, dg[i], du[i], p);
+                Vec<T, VEC>::store(dgp + row * dgs + c, dg);
+                Vec<T, VEC>::store(dup + row * dus + c, du);
+            }
+            if constexpr (WANT_DS) {
+                const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                const float w = wave_sum(p);
+                if (lane == 0)
+                    part_ds[((int64_t)blockIdx.x * kWaves + wave) * G.total_rows + G.row0 + row] = w;
+            }
+        };
+        one_row(r0, g0, u0, d0, s0);
+        if (two) one_row(r0 + 1, g1, u1, d1, s1);
+        return;
+    }
     const int64_t row = blockIdx.y;
     const uint32_t col = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
     const bool active = col < G.nv;
@@ -489,7 +541,7 @@ swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
         y = const_cast<T*>(static_cast<const T*>(ops[2].p)) + r0 * ys;
         sc = A.scale != nullptr ? A.scale + r0 * scs : nullptr;
         G.rows = rc;
-        const uint32_t gy = (uint32_t)(hb && kFwdBiasRows == 2 ? (rc + 1) / 2 : rc);
+        const uint32_t gy = (uint32_t)(hb && kBiasRows == 2 ? (rc + 1) / 2 : rc);
         const dim3 grid = P.wide ? dim3(P.tiles, gy)
                                  : dim3(swiglu_host::flat_blocks(rc, P.nv, kBlock), 1);
         if (hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream) != hipSuccess)
@@ -604,7 +656,10 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
         G.row0 = r0;
         G.group0 = r0 / kBsRows;
         if (one_shot) {
-            if (hipLaunchKernel(k1, dim3(tiles, (uint32_t)rc), dim3(kBlock), args1, 0, stream) !=
+            // with a bias, a block takes two rows (see the kernel)
+            const uint32_t gy =
+                (uint32_t)(bg != nullptr && kBiasRows == 2 ? (rc + 1) / 2 : rc);
+            if (hipLaunchKernel(k1, dim3(tiles, gy), dim3(kBlock), args1, 0, stream) !=
                 hipSuccess)
                 return SWIGLU_ERR_HIP;
             continue;
