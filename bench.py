@@ -238,19 +238,18 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
         xbuf = torch.empty(tokens, 2 * n, dtype=torch.bfloat16, device=dev)
         flops = 2.0 * tokens * hidden * 2 * n
 
-        def timed(fn, warmup=5):
-            # (a longer warm-up than the streaming legs: the first launches of
-            # a matrix-core kernel run while the clocks are still ramping)
-            ts = []
+        def timed(fn, warmup=20):
+            # back to back on the stream, one synchronisation at the end (so
+            # the GPU never idles between launches); mean of the timed ones
+            ev = []
             for k in range(iters + warmup):
                 s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s0.record(stream)
                 fn()
                 s1.record(stream)
-                s1.synchronize()
-                if k >= warmup:
-                    ts.append(s0.elapsed_time(s1))
-            return float(np.mean(ts))
+                ev.append((s0, s1))
+            ev[-1][1].synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in ev[warmup:]]))
 
         if si == 0:
             # Untimed: sustained matrix-core load until the clocks have
