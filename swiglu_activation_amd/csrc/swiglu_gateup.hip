@@ -15,11 +15,13 @@
 //    computes in fp32 registers and stores the result vectors. Consecutive
 //    lanes own consecutive vectors, so each wave64 load or store covers 1 KiB
 //    of contiguous memory.
-//  * The grid is one-shot and 2D: blockIdx.y picks a row (or, for rows
-//    narrower than a block, a group of rows), blockIdx.x a 256-vector column
-//    tile. Row offsets are uniform per block and live in scalar registers; no
-//    lane divides. Enough blocks are in flight that HBM stays saturated
-//    (131072 blocks for 8192 x 32768 bf16).
+//  * The grid is one-shot. Wide rows (at least 256 vectors per half row):
+//    blockIdx.y picks a row and blockIdx.x a 256-vector column tile; row
+//    offsets are uniform per block and live in scalar registers, and no lane
+//    divides. Narrow rows: a flat 1D grid over the (row, vector) lanes, each
+//    lane finding its row with one fp64 multiply, so no lane idles. Enough
+//    blocks are in flight that HBM stays saturated (131072 blocks for
+//    8192 x 32768 bf16).
 //  * Loads and stores carry the nontemporal hint: nothing is re-read, and
 //    keeping the stream out of the caches measured faster on large shapes.
 //  * Arithmetic is kept short because at 16 bytes per lane the forward has
