@@ -434,7 +434,10 @@ def swiglu_fc1_fwd(a, w, y=None, *, x_out=None, stream=None):
     """y = silu(a @ w[:n].T) * (a @ w[n:].T) for bf16 a [..., k] and w [2n, k].
 
     x_out: None, True (allocate) or a [..., 2n] tensor that receives a @ w.T.
-    Returns y, or (y, x_out) when x_out is requested."""
+    Returns y, or (y, x_out) when x_out is requested. n and k must be
+    multiples of 64, rows 16-byte aligned, and the row strides of a and w at
+    most 2^28 elements; anything else raises ValueError (the C entry point's
+    status)."""
     import torch
     lib = load_library()
     _require_device(a, w, y, x_out if isinstance(x_out, torch.Tensor) else None)
