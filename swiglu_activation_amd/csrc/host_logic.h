@@ -55,11 +55,15 @@ inline bool views_overlap(Operand a, int64_t wa, Operand b, int64_t wb, int64_t 
 }
 
 // Largest per-lane access (16, 8, 4 or 2 bytes; at least one element) that
-// every operand's base pointer and row stride are aligned to.
-inline int vec_bytes(int esz, const Operand* ops, int nops) {
+// every operand's base pointer and row stride are aligned to and that divides
+// the row width of n elements, so that n / VEC vectors cover every column of
+// every operand (the views of a two-tensor call may be padded rows of wider
+// buffers, where n need not be a multiple of the widest access the pointers
+// and strides allow).
+inline int vec_bytes(int esz, int64_t n, const Operand* ops, int nops) {
     int b = 16;
     for (; b > esz; b >>= 1) {
-        bool ok = true;
+        bool ok = ((n * esz) % b) == 0;
         for (int i = 0; i < nops; ++i)
             ok = ok && ((uintptr_t)ops[i].p % (uintptr_t)b) == 0 && ((ops[i].stride * esz) % b) == 0;
         if (ok) break;
@@ -67,13 +71,12 @@ inline int vec_bytes(int esz, const Operand* ops, int nops) {
     return b;
 }
 
-// Launch plan. WIDE (n/VEC >= block): block (x, y) owns vectors
-// [x*block, (x+1)*block) of row y. Narrow: block y owns rpb = block / nv
-// whole rows. Rows are covered by launches of at most max_grid_y row groups.
-// Launch plan. Wide rows (at least `block` vectors per half row): a 2D grid
-// of (column tile, row) blocks. Narrow rows: a flat 1D grid over the linear
-// (row, vector) index space, so no lane idles except in the last block; one
-// launch covers at most 2^31 lanes.
+// Launch plan for rows of n elements accessed VEC at a time (VEC divides n,
+// as vec_bytes guarantees). Wide rows (at least `block` vectors per half
+// row): a 2D grid of (column tile, row) blocks. Narrow rows: a flat 1D grid
+// over the linear (row, vector) index space, so no lane idles except in the
+// last block; one launch covers at most 2^31 lanes. A plan with nv == 0
+// (n == 0, never launched) has rows_per_launch 0.
 struct Plan {
     bool wide;
     uint32_t nv;                 // vectors per half row
@@ -88,7 +91,8 @@ inline Plan make_plan(int64_t n, int vec, uint32_t block, uint32_t max_grid_y) {
     P.nv = (uint32_t)(n / vec);
     P.wide = P.nv >= block;
     P.tiles = P.wide ? (P.nv + block - 1) / block : 0u;
-    P.rows_per_launch = P.wide ? (int64_t)max_grid_y : kFlatLanes / P.nv;
+    if (P.nv == 0) P.rows_per_launch = 0;
+    else P.rows_per_launch = P.wide ? (int64_t)max_grid_y : kFlatLanes / P.nv;
     return P;
 }
 

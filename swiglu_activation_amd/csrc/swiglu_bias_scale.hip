@@ -534,6 +534,7 @@ swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
     G.nv = P.nv;
     G.inv_nv = 1.0 / (double)P.nv;
     void* args[] = {&g, &gs, &u, &us, &y, &ys, &bg, &bu, &sc, &scs, &G};
+    if (P.rows_per_launch <= 0) return SWIGLU_ERR_BAD_SHAPE;   // n == 0 is never planned
     for (int64_t r0 = 0; r0 < rows; r0 += P.rows_per_launch) {
         const int64_t rc = rows - r0 < P.rows_per_launch ? rows - r0 : P.rows_per_launch;
         g = static_cast<const T*>(ops[0].p) + r0 * gs;
@@ -712,7 +713,7 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_fw
     const BsArgs A{bias, scale, scale_stride};
     const Operand ops[5] = {ox, Operand{offset(x, n, esz), x_row_stride}, oy,
                             Operand{bias, 0}, Operand{offset(bias, n, esz), 0}};
-    const int vb = vec_bytes((int)esz, ops, bias != nullptr ? 5 : 3);
+    const int vb = vec_bytes((int)esz, n, ops, bias != nullptr ? 5 : 3);
     if (dtype == SWIGLU_DTYPE_BF16) {
         switch (vb) {
             case 16: return fwd_bs_launch<uint16_t, 8>(ops, A, rows, n, stream);
@@ -795,7 +796,7 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bw
     const Operand ops[7] = {ody, ox, Operand{offset(x, n, esz), x_row_stride}, odx,
                             Operand{offset(dx, n, esz), dx_row_stride}, Operand{bias, 0},
                             Operand{offset(bias, n, esz), 0}};
-    const int vb = vec_bytes((int)esz, ops, bias != nullptr ? 7 : 5);
+    const int vb = vec_bytes((int)esz, n, ops, bias != nullptr ? 7 : 5);
 #define SWIGLU_BWD_BS(T, V)                                                                  \
     bwd_bs_launch<T, V>(ops, A, rows, n, ip, dbias, dscale, dscale_stride, workspace, stream)
     if (dtype == SWIGLU_DTYPE_BF16) {

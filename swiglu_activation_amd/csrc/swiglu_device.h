@@ -222,11 +222,7 @@ __device__ __forceinline__ float h_factor_lo(float z, float zlo, float osig) {
 }
 
 // ---------------------------------------------------------------------------
-// Launch geometry. WIDE (n/VEC >= kBlock): block (x, y) owns vectors
-// [x*kBlock, (x+1)*kBlock) of row y. Narrow: block y owns rpb whole rows;
-// lane t takes row t / nv, vector t % nv, computed once in fp32 (exact: both
-// operands are below 256 and the quotient is never within 1/512 of an
-// integer).
+// Launch geometry (the mapping is described at locate() below).
 // ---------------------------------------------------------------------------
 struct Geom {
     int64_t rows;     // rows covered by this launch

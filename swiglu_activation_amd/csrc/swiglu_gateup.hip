@@ -115,6 +115,7 @@ swiglu_status launch_chunks(const void* kernel, const Plan& P, int64_t rows, con
         args[2 * i + 1] = &stride[i];
     }
     args[2 * NOPS] = &G;
+    if (P.rows_per_launch <= 0) return SWIGLU_ERR_BAD_SHAPE;   // n == 0 is never planned
     G.nv = P.nv;
     G.inv_nv = 1.0 / (double)P.nv;
     for (int64_t r0 = 0; r0 < rows; r0 += P.rows_per_launch) {
@@ -159,7 +160,7 @@ swiglu_status run_fwd(Operand gate, Operand up, Operand y, int64_t rows, int64_t
                       swiglu_dtype dtype, hipStream_t stream) {
     const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
     const Operand ops[3] = {gate, up, y};
-    const int vb = vec_bytes((int)esz, ops, 3);
+    const int vb = vec_bytes((int)esz, n, ops, 3);
     if (dtype == SWIGLU_DTYPE_BF16) {
         switch (vb) {
             case 16: return fwd_launch<uint16_t, 8>(ops, rows, n, stream);
@@ -181,7 +182,7 @@ swiglu_status run_bwd(Operand dy, Operand gate, Operand up, Operand dgate, Opera
                       hipStream_t stream) {
     const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
     const Operand ops[5] = {dy, gate, up, dgate, dup};
-    const int vb = vec_bytes((int)esz, ops, 5);
+    const int vb = vec_bytes((int)esz, n, ops, 5);
     if (dtype == SWIGLU_DTYPE_BF16) {
         switch (vb) {
             case 16: return bwd_launch<uint16_t, 8>(ops, rows, n, in_place, stream);

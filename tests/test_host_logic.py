@@ -27,14 +27,22 @@ int main() {
             std::scanf("%llu %lld %lld %llu %lld %lld %lld %lld", &pa, &sa, &wa, &pb, &sb, &wb, &rows, &esz);
             Operand a{(const void*)(uintptr_t)pa, sa}, b{(const void*)(uintptr_t)pb, sb};
             std::printf("%d\n", views_overlap(a, wa, b, wb, rows, esz) ? 1 : 0);
-        } else if (op == 'v') {
-            int esz, nops; std::scanf("%d %d", &esz, &nops);
+        } else if (op == 'v' || op == 'c') {
+            // 'v': the access width; 'c': the columns the plan's vectors cover
+            int esz, nops; long long n; std::scanf("%d %lld %d", &esz, &n, &nops);
             Operand ops[8];
             for (int i = 0; i < nops; ++i) {
                 unsigned long long p; long long s; std::scanf("%llu %lld", &p, &s);
                 ops[i] = Operand{(const void*)(uintptr_t)p, s};
             }
-            std::printf("%d\n", vec_bytes(esz, ops, nops));
+            const int vb = vec_bytes(esz, n, ops, nops);
+            if (op == 'v') {
+                std::printf("%d\n", vb);
+            } else {
+                const int vec = vb / esz;
+                Plan P = make_plan(n, vec, 256, 65535);
+                std::printf("%d %lld %lld\n", vec, (long long)P.nv * vec, (long long)P.rows_per_launch);
+            }
         } else if (op == 'p') {
             long long n; int vec; unsigned block, maxgy;
             std::scanf("%lld %d %u %u", &n, &vec, &block, &maxgy);
@@ -125,13 +133,63 @@ def test_packed_halves_do_not_overlap(driver):
 
 def test_vec_bytes(driver):
     got = driver([
-        "v 2 3 4096 8 8192 16 12288 8",      # all 16-byte aligned
-        "v 2 2 4098 8 8192 16",              # pointer 2-byte aligned
-        "v 2 2 4096 12 8192 16",             # stride 24 bytes -> 8
-        "v 4 2 4096 3 8192 4",               # fp32 stride 12 bytes -> 4
-        "v 2 1 4100 8",                      # pointer 4-byte aligned
+        "v 2 8 3 4096 8 8192 16 12288 8",    # all 16-byte aligned
+        "v 2 8 2 4098 8 8192 16",            # pointer 2-byte aligned
+        "v 2 8 2 4096 12 8192 16",           # stride 24 bytes -> 8
+        "v 4 4 2 4096 3 8192 4",             # fp32 stride 12 bytes -> 4
+        "v 2 8 1 4100 8",                    # pointer 4-byte aligned
+        # padded two-tensor views: pointers and strides 16-byte aligned, but
+        # the row width n is not a multiple of 16 bytes
+        "v 4 5 3 4096 8 8192 8 12288 8",     # fp32 n=5 in rows of 8 -> 4 bytes
+        "v 4 3 3 4096 4 8192 4 12288 4",     # fp32 n=3 in rows of 4 -> 4 bytes
+        "v 2 12 3 4096 16 8192 16 12288 16",  # bf16 n=12 in rows of 16 -> 8 bytes
+        "v 4 6 2 4096 8 8192 8",             # fp32 n=6 -> 8 bytes
+        "v 2 1 2 4096 8 8192 8",             # bf16 n=1 -> one element
     ])
-    assert got == ["16", "2", "8", "4", "4"]
+    assert got == ["16", "2", "8", "4", "4", "4", "4", "8", "8", "2"]
+
+
+def test_plan_covers_every_column(driver):
+    """For every n in [1, 300], both element sizes, and pointers and strides
+    aligned to 16, 8, 4 or 2 bytes (two or five operands, as the two-tensor
+    forward and backward pass them), the chosen vectors cover exactly n
+    columns and the width divides every operand's alignment (brute force over
+    the definition of the access width)."""
+    rng = np.random.default_rng(11)
+    cases, want = [], []
+    for esz in (2, 4):
+        for n in range(1, 301):
+            for _ in range(4):
+                nops = int(rng.choice([2, 3, 5]))
+                ops = []
+                for _ in range(nops):
+                    pal = int(rng.choice([16, 8, 4, 2]))
+                    pal = max(pal, esz)
+                    p = 1 << 20
+                    p += pal if rng.random() < 0.5 else 0           # aligned to pal exactly
+                    p -= p % esz
+                    extra = int(rng.integers(0, 9))
+                    s = n + extra
+                    ops.append((p, s))
+                line = f"c {esz} {n} {nops} " + " ".join(f"{p} {s}" for p, s in ops)
+                cases.append(line)
+                # brute force: the largest b in {16, 8, 4, 2} (b >= esz) with
+                # every pointer, every stride*esz and n*esz divisible by b
+                b = esz
+                for cand in (16, 8, 4):
+                    if cand < esz:
+                        continue
+                    if (n * esz) % cand == 0 and all(p % cand == 0 and (s * esz) % cand == 0
+                                                     for p, s in ops):
+                        b = cand
+                        break
+                want.append(b // esz)
+    got = driver(cases)
+    for line, g, vec in zip(cases, got, want):
+        gv, covered, rpl = (int(t) for t in g.split())
+        assert gv == vec, line
+        assert covered == int(line.split()[2]), line     # nv * VEC == n
+        assert rpl > 0, line
 
 
 def test_launch_plan(driver):
