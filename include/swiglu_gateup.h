@@ -20,7 +20,9 @@
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers on the current HIP device. The caller owns
  *    every buffer; the library allocates nothing, frees nothing, keeps no
- *    per-call state, and never synchronizes.
+ *    per-call state, and never synchronizes. (The one static buffer, the
+ *    scratch of swiglu_gateup_bias_scale_bwd_noalloc, is part of the
+ *    library's code object on each GPU, not an allocation made by a call.)
  *  - Row strides are counted in ELEMENTS (not bytes); columns are contiguous
  *    (unit stride). A row stride larger than the row's width is allowed (for
  *    example a view into a wider buffer); the columns past the width are never
@@ -64,7 +66,9 @@ typedef enum {
     SWIGLU_ERR_BAD_DTYPE = 4,     /* dtype is neither SWIGLU_DTYPE_F32 nor SWIGLU_DTYPE_BF16 */
     SWIGLU_ERR_ALIASING = 5,      /* outputs overlap inputs where that is not allowed */
     SWIGLU_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
-    SWIGLU_ERR_WORKSPACE = 7      /* a needed workspace is NULL, too small or not 16-byte aligned */
+    SWIGLU_ERR_WORKSPACE = 7,     /* a needed workspace is NULL, too small or not 16-byte aligned */
+    SWIGLU_ERR_SCRATCH_LIMIT = 8  /* the problem needs more than the static scratch holds
+                                     (swiglu_gateup_bias_scale_bwd_noalloc only) */
 } swiglu_status;
 
 /*
@@ -236,6 +240,43 @@ swiglu_status swiglu_gateup_bias_scale_bwd(const void* dy, int64_t dy_row_stride
                                            void* workspace, size_t workspace_bytes,
                                            int64_t rows, int64_t n,
                                            swiglu_dtype dtype, int in_place, hipStream_t stream);
+
+/*
+ * Allocation-free variant of swiglu_gateup_bias_scale_bwd, for callers that
+ * cannot allocate device memory or pass a workspace: code recorded under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results and bits as swiglu_gateup_bias_scale_bwd, without
+ * workspace and workspace_bytes: the partial sums go to a static device array
+ * of SWIGLU_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU
+ * it runs on until the process ends (its address is looked up once per
+ * device, on the first call there). The call allocates and frees nothing.
+ *
+ *   Limit: swiglu_gateup_bias_scale_workspace_size(rows, n, dbias != NULL,
+ *   dscale != NULL) must not exceed SWIGLU_NOALLOC_SCRATCH_BYTES; larger
+ *   problems return SWIGLU_ERR_SCRATCH_LIMIT before anything is launched.
+ *   (8192 rows of n = 32768 with both sums need 32 MiB.)
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls on
+ *   one GPU that may overlap in time (different streams, or different host
+ *   threads without ordering) race and must not be issued. The array needs
+ *   no clearing: every partial is written before it is read.
+ *
+ * Errors: those of swiglu_gateup_bias_scale_bwd except SWIGLU_ERR_WORKSPACE;
+ * also SWIGLU_ERR_SCRATCH_LIMIT, and SWIGLU_ERR_HIP when the array's device
+ * address cannot be obtained.
+ */
+#define SWIGLU_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+swiglu_status swiglu_gateup_bias_scale_bwd_noalloc(const void* dy, int64_t dy_row_stride,
+                                                   void* x, int64_t x_row_stride,
+                                                   const void* bias, const float* scale,
+                                                   int64_t scale_stride,
+                                                   void* dx, int64_t dx_row_stride,
+                                                   float* dbias, float* dscale,
+                                                   int64_t dscale_stride,
+                                                   int64_t rows, int64_t n,
+                                                   swiglu_dtype dtype, int in_place,
+                                                   hipStream_t stream);
 
 /*
  * fc1 projection with the SwiGLU as its epilogue (Liger-Kernel Megatron

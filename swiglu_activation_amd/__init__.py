@@ -18,8 +18,9 @@ import os
 
 __all__ = ["swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
            "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
-           "swiglu_gateup_bias_scale_workspace_size", "swiglu_fc1_fwd", "swiglu_status_string",
-           "SwiGLUError", "library_path", "load_library", "EXPORTS"]
+           "swiglu_gateup_bias_scale_workspace_size", "swiglu_gateup_bias_scale_bwd_noalloc",
+           "swiglu_fc1_fwd", "swiglu_status_string", "SwiGLUError", "library_path",
+           "load_library", "EXPORTS", "NOALLOC_SCRATCH_BYTES"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG_DIR, "libswiglu_gateup.so")
@@ -33,13 +34,16 @@ SWIGLU_ERR_BAD_DTYPE = 4
 SWIGLU_ERR_ALIASING = 5
 SWIGLU_ERR_HIP = 6
 SWIGLU_ERR_WORKSPACE = 7
+SWIGLU_ERR_SCRATCH_LIMIT = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20     # SWIGLU_NOALLOC_SCRATCH_BYTES of the header
 SWIGLU_DTYPE_F32 = 0
 SWIGLU_DTYPE_BF16 = 1
 _BAD_DTYPE_CODE = -1    # passed for any other torch dtype; the library rejects it
 
 EXPORTS = ("swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
            "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
-           "swiglu_gateup_bias_scale_workspace_size", "swiglu_fc1_fwd", "swiglu_status_string")
+           "swiglu_gateup_bias_scale_workspace_size", "swiglu_gateup_bias_scale_bwd_noalloc",
+           "swiglu_fc1_fwd", "swiglu_status_string")
 
 _lib = None
 
@@ -87,6 +91,9 @@ def load_library():
     lib.swiglu_gateup_bias_scale_bwd.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp,
                                                  i64, vp, ctypes.c_size_t, i64, i64, cint, cint, vp]
     lib.swiglu_gateup_bias_scale_bwd.restype = cint
+    lib.swiglu_gateup_bias_scale_bwd_noalloc.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64,
+                                                         vp, vp, i64, i64, i64, cint, cint, vp]
+    lib.swiglu_gateup_bias_scale_bwd_noalloc.restype = cint
     lib.swiglu_fc1_fwd.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, cint, vp]
     lib.swiglu_fc1_fwd.restype = cint
     lib.swiglu_status_string.argtypes = [cint]
@@ -423,6 +430,53 @@ def swiglu_gateup_bias_scale_bwd(dy, x, bias=None, scale=None, dx=None, *, want_
             dbias.data_ptr() if dbias is not None else None, dsp, dss, wp, wb, rows, n,
             _dtype_code(x), 1 if in_place else 0, _stream_handle(x.device, stream))
     _check(st, "swiglu_gateup_bias_scale_bwd")
+    return out, dbias, dscale
+
+
+def swiglu_gateup_bias_scale_bwd_noalloc(dy, x, dx=None, dbias=None, dscale=None, *, bias=None,
+                                         scale=None, in_place: bool = False, stream=None):
+    """swiglu_gateup_bias_scale_bwd without any allocation: the caller passes
+    every output (dx, unless in_place; dbias [2n] float32 to get dbias;
+    dscale float32 shaped like scale to get dscale) and the partial sums go to
+    the library's static per-GPU scratch. Calls that may overlap in time on
+    one GPU race on that scratch. Problems needing more than
+    NOALLOC_SCRATCH_BYTES of partials raise (SWIGLU_ERR_SCRATCH_LIMIT).
+    Returns (dx or x, dbias, dscale)."""
+    lib = load_library()
+    _require_device(dy, x, dx, dbias, dscale)
+    if x.dim() < 1 or x.shape[-1] % 2:
+        raise ValueError("last dimension of x must be even (2n)")
+    n = x.shape[-1] // 2
+    if dy.dtype != x.dtype:
+        raise ValueError("dy and x must have the same dtype")
+    rows, xs = _rows_and_stride(x, "x")
+    dys = _same_rows(dy, rows, n, "dy")
+    bp = _bias_arg(bias, x, n)
+    sp, ss = _per_row_arg(scale, x, rows, "scale")
+    if dbias is not None:
+        import torch
+        if dbias.dtype != torch.float32 or dbias.dim() != 1 or dbias.shape[0] != 2 * n or \
+                (n and dbias.stride(0) != 1):
+            raise ValueError(f"dbias must be a contiguous float32 [{2 * n}] tensor")
+    dsp, dss = _per_row_arg(dscale, x, rows, "dscale") if dscale is not None else (None, 1)
+    if in_place:
+        if dx is not None and dx.data_ptr() != x.data_ptr():
+            raise ValueError("in_place backward writes into x; pass dx=None or dx=x")
+        dx_ptr, dxs, out = None, 0, x
+    else:
+        if dx is None:
+            raise ValueError("the allocation-free backward needs dx (or in_place=True)")
+        if dx.dtype != x.dtype:
+            raise ValueError("dx and x must have the same dtype")
+        dxs = _same_rows(dx, rows, 2 * n, "dx")
+        dx_ptr, out = dx.data_ptr(), dx
+    import torch
+    with torch.cuda.device(x.device):
+        st = lib.swiglu_gateup_bias_scale_bwd_noalloc(
+            dy.data_ptr(), dys, x.data_ptr(), xs, bp, sp, ss, dx_ptr, dxs,
+            dbias.data_ptr() if dbias is not None else None, dsp, dss, rows, n,
+            _dtype_code(x), 1 if in_place else 0, _stream_handle(x.device, stream))
+    _check(st, "swiglu_gateup_bias_scale_bwd_noalloc")
     return out, dbias, dscale
 
 

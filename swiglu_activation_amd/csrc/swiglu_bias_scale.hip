@@ -10,6 +10,8 @@
 // results are bitwise deterministic.
 #include "swiglu_device.h"
 
+#include <mutex>
+
 namespace {
 
 using namespace swiglu_impl;
@@ -729,11 +731,46 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_fw
     }
 }
 
-__attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bwd(
-    const void* dy, int64_t dy_row_stride, void* x, int64_t x_row_stride, const void* bias,
-    const float* scale, int64_t scale_stride, void* dx, int64_t dx_row_stride, float* dbias,
-    float* dscale, int64_t dscale_stride, void* workspace, size_t workspace_bytes, int64_t rows,
-    int64_t n, swiglu_dtype dtype, int in_place, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free backward: a file-scope device array
+// that every GPU the library runs on holds until the process ends. In host
+// code `scratch` names a host-side stand-in, not device memory, so it is
+// never passed to a kernel or a copy: its device address is looked up once
+// per device (with that device current) and the looked-up pointer is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SWIGLU_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once looked up
+
+// Device address of `scratch` on the current device.
+swiglu_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SWIGLU_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return SWIGLU_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SWIGLU_OK;
+}
+
+// The backward with its partial sums in `workspace` (caller's), or, with
+// use_static, in the static scratch (workspace and workspace_bytes unused).
+swiglu_status bias_scale_bwd(const void* dy, int64_t dy_row_stride, void* x, int64_t x_row_stride,
+                             const void* bias, const float* scale, int64_t scale_stride, void* dx,
+                             int64_t dx_row_stride, float* dbias, float* dscale,
+                             int64_t dscale_stride, void* workspace, size_t workspace_bytes,
+                             bool use_static, int64_t rows, int64_t n, swiglu_dtype dtype,
+                             int in_place, hipStream_t stream) {
     swiglu_status st = check_shape(rows, n, dtype);
     if (st != SWIGLU_OK) return st;
     const int64_t esz = dtype == SWIGLU_DTYPE_F32 ? 4 : 2;
@@ -760,8 +797,13 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bw
     }
     if (!dy || !x || !dx) return SWIGLU_ERR_NULL_POINTER;
     const size_t need = bs_workspace_bytes(rows, n, dbias != nullptr, dscale != nullptr);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need || (uintptr_t)workspace % 16))
+    if (use_static) {
+        if (need > SWIGLU_NOALLOC_SCRATCH_BYTES) return SWIGLU_ERR_SCRATCH_LIMIT;
+        workspace = nullptr;           // looked up after validation, just before the launch
+    } else if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                            (uintptr_t)workspace % 16)) {
         return SWIGLU_ERR_WORKSPACE;
+    }
 
     const Operand ody{dy, dy_row_stride}, ox{x, x_row_stride}, odx{dx, dx_row_stride};
     if (views_overlap(ody, n, ox, 2 * n, rows, esz)) return SWIGLU_ERR_ALIASING;
@@ -784,13 +826,17 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bw
     outs[nout++] = span_of(odx, rows, 2 * n, esz);
     if (dbias != nullptr) outs[nout++] = span_of(Operand{dbias, 2 * n}, 1, 2 * n, 4);
     if (dscale != nullptr) outs[nout++] = span_of(Operand{dscale, dscale_stride}, rows, 1, 4);
-    if (need > 0) outs[nout++] = Span{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (need > 0 && !use_static)       // the static array is no caller's memory
+        outs[nout++] = Span{(uintptr_t)workspace, (uintptr_t)workspace + need};
     for (int i = 0; i < nout; ++i) {
         for (int j = (i == 0 ? 2 - (ip ? 1 : 0) : 0); j < nin; ++j)   // dx vs dy/x: checked above
             if (spans_overlap(outs[i], ins[j])) return SWIGLU_ERR_ALIASING;
         for (int j = i + 1; j < nout; ++j)
             if (spans_overlap(outs[i], outs[j])) return SWIGLU_ERR_ALIASING;
     }
+
+    if (use_static && need > 0 && (st = scratch_on_current_device(&workspace)) != SWIGLU_OK)
+        return st;
 
     const BsArgs A{bias, scale, scale_stride};
     const Operand ops[7] = {ody, ox, Operand{offset(x, n, esz), x_row_stride}, odx,
@@ -813,6 +859,30 @@ __attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bw
         default: return SWIGLU_BWD_BS(float, 1);
     }
 #undef SWIGLU_BWD_BS
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bwd(
+    const void* dy, int64_t dy_row_stride, void* x, int64_t x_row_stride, const void* bias,
+    const float* scale, int64_t scale_stride, void* dx, int64_t dx_row_stride, float* dbias,
+    float* dscale, int64_t dscale_stride, void* workspace, size_t workspace_bytes, int64_t rows,
+    int64_t n, swiglu_dtype dtype, int in_place, hipStream_t stream) {
+    return bias_scale_bwd(dy, dy_row_stride, x, x_row_stride, bias, scale, scale_stride, dx,
+                          dx_row_stride, dbias, dscale, dscale_stride, workspace, workspace_bytes,
+                          false, rows, n, dtype, in_place, stream);
+}
+
+__attribute__((visibility("default"))) swiglu_status swiglu_gateup_bias_scale_bwd_noalloc(
+    const void* dy, int64_t dy_row_stride, void* x, int64_t x_row_stride, const void* bias,
+    const float* scale, int64_t scale_stride, void* dx, int64_t dx_row_stride, float* dbias,
+    float* dscale, int64_t dscale_stride, int64_t rows, int64_t n, swiglu_dtype dtype,
+    int in_place, hipStream_t stream) {
+    return bias_scale_bwd(dy, dy_row_stride, x, x_row_stride, bias, scale, scale_stride, dx,
+                          dx_row_stride, dbias, dscale, dscale_stride, nullptr, 0, true, rows, n,
+                          dtype, in_place, stream);
 }
 
 }  // extern "C"

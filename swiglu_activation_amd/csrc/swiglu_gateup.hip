@@ -214,6 +214,8 @@ __attribute__((visibility("default"))) const char* swiglu_status_string(swiglu_s
         case SWIGLU_ERR_ALIASING: return "SWIGLU_ERR_ALIASING: output overlaps an input";
         case SWIGLU_ERR_HIP: return "SWIGLU_ERR_HIP: HIP runtime or launch failure";
         case SWIGLU_ERR_WORKSPACE: return "SWIGLU_ERR_WORKSPACE: workspace missing, too small or misaligned";
+        case SWIGLU_ERR_SCRATCH_LIMIT:
+            return "SWIGLU_ERR_SCRATCH_LIMIT: the problem needs more than the static scratch holds";
     }
     return "SWIGLU_ERR_UNKNOWN: not a swiglu_status value";
 }
