@@ -324,7 +324,7 @@ def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
                            "what": "no bias, per-token scale; bwd writes dx and dscale"}}
 
 
-def configs_leg(dev, stream, skip: str, replays: int = 10):
+def configs_leg(dev, stream, names, replays: int = 20, parity_rows: int = 512):
     """Every other workload's forward and backward (in place where the
     workload says so), as context for the headline: device-drawn inputs of
     the workload's shape and dtype (timing does not depend on the values),
@@ -332,16 +332,27 @@ def configs_leg(dev, stream, skip: str, replays: int = 10):
     more than 512 MB earlier, so the 256 MB Infinity Cache cannot serve it.
     The launches over all sets are captured in one HIP graph per pass and the
     graph is replayed, so host launch overhead does not show in the times of
-    the short kernels (these workloads run 3 to 140 us per launch)."""
+    the short kernels (these workloads run 2 to 420 us per launch). A graph
+    holds at least 32 launches; each figure is the per-launch time, median
+    over `replays` replays, with the min and max.
+
+    The last `parity_rows` rows of the first set hold the workload's own
+    recipe (synth), and the timed launches' outputs of those rows are kept
+    (the in-place backward's input rows are restored before its last replay),
+    for the oracle comparison in the CPU-baseline leg.
+
+    Beside each pass, a zero-arithmetic stream of the same bytes (one-shot
+    grid of 256 lanes over separate flat streams, same rotation and graph
+    replay) gives what the memory system allows at that size."""
     import numpy as np
     import torch
 
+    import ceiling
     import synth
     import swiglu_activation_amd as sw
-    out = {}
-    for w in synth.WORKLOADS.values():
-        if w.name == skip:
-            continue
+    out, samples = {}, {}
+    for name in names:
+        w = synth.WORKLOADS[name]
         tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         e = w.elem_bytes
         fwd_bytes, bwd_bytes = 3 * e * w.rows * w.n, 5 * e * w.rows * w.n
@@ -355,20 +366,44 @@ def configs_leg(dev, stream, skip: str, replays: int = 10):
             y = torch.empty(w.shape[:-1] + (w.n,), dtype=tdt, device=dev)
             dx = None if w.in_place else torch.empty_like(x)
             bufs.append((x, dy, y, dx))
+        r0 = max(0, w.rows - parity_rows)
+        xs_h, dys_h = synth.make_x(w, r0, w.rows), synth.make_dy(w, r0, w.rows)
+
+        def dev_rows(a):
+            if w.dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        def host_rows(t, cols):
+            a = t.reshape(w.rows, cols)[r0:]
+            if w.dtype == "bf16":
+                return a.view(torch.int16).cpu().numpy().view(np.uint16)
+            return a.cpu().numpy()
+
+        x0_rows = bufs[0][0].view(w.rows, 2 * w.n)[r0:]
+        x0_rows.copy_(dev_rows(xs_h))
+        bufs[0][1].view(w.rows, w.n)[r0:].copy_(dev_rows(dys_h))
+        torch.cuda.synchronize()
+
+        # Launch order of one graph: at least 32 launches cycling over sets
+        # 1.. (each set's data last touched more than 512 MB earlier), then
+        # set 0, which holds the sampled rows, once, last.
+        order = [1 + i % (sets - 1) for i in range(max(sets - 1, 32))] + [0]
 
         def fwd_pass():
-            for x, dy, y, dx in bufs:
+            for i in order:
+                x, dy, y, dx = bufs[i]
                 sw.swiglu_gateup_fwd(x, y)
 
         def bwd_pass():
-            for x, dy, y, dx in bufs:
+            for i in order:
+                x, dy, y, dx = bufs[i]
                 if w.in_place:
                     sw.swiglu_gateup_bwd(dy, x, in_place=True)
                 else:
                     sw.swiglu_gateup_bwd(dy, x, dx)
 
-        res = {}
-        for name, fn, nbytes in (("fwd", fwd_pass, fwd_bytes), ("bwd", bwd_pass, bwd_bytes)):
+        def replayed(fn, before_last=None):
             fn()                                              # warm up outside the graph
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
@@ -377,22 +412,167 @@ def configs_leg(dev, stream, skip: str, replays: int = 10):
             g.replay()
             torch.cuda.synchronize()
             ts = []
-            for _ in range(replays):
+            for i in range(replays):
+                if before_last is not None and i == replays - 1:
+                    before_last()
+                    torch.cuda.synchronize()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 g.replay()
                 b.record(stream)
                 b.synchronize()
-                ts.append(a.elapsed_time(b) / sets)
-            t = float(np.median(ts))
-            res[f"{name}_us"] = round(t * 1e3, 2)
-            res[f"{name}_GBps"] = round(nbytes / t / 1e6, 1)
+                ts.append(a.elapsed_time(b) / len(order))
             del g
-        res.update({"bwd": "in place" if w.in_place else "out of place", "buffer_sets": sets,
-                    "timing": "HIP graph of one launch per buffer set, replayed"})
-        out[w.name] = res
+            return float(np.median(ts)), min(ts), max(ts)
+
+        res = {}
+        sample = {"rows": [r0, w.rows], "x": xs_h, "dy": dys_h}
+        for pname, fn, nbytes in (("fwd", fwd_pass, fwd_bytes), ("bwd", bwd_pass, bwd_bytes)):
+            restore = (lambda: x0_rows.copy_(dev_rows(xs_h))) if (w.in_place and pname == "bwd") \
+                else None
+            t, tmin, tmax = replayed(fn, restore)
+            res[f"{pname}_us"] = round(t * 1e3, 2)
+            res[f"{pname}_us_min_max"] = [round(tmin * 1e3, 2), round(tmax * 1e3, 2)]
+            res[f"{pname}_GBps"] = round(nbytes / t / 1e6, 1)
+            if pname == "fwd":
+                sample["y"] = host_rows(bufs[0][2], w.n)
+            else:
+                sample["dx"] = host_rows(bufs[0][0] if w.in_place else bufs[0][3], 2 * w.n)
         del bufs
-    return out
+        # the same bytes with no arithmetic, independent structure
+        if (w.n * e) % 16 == 0:
+            nvec = w.rows * w.n * e // 16
+            fsets = [ceiling.FlatStreams(nvec, dev) for _ in range(sets)]
+            for pname, mix, nbytes in (("fwd", "fwd", fwd_bytes), ("bwd", "bwd", bwd_bytes)):
+                t, _, _ = replayed(lambda: [ceiling.probe(0, mix, fsets[i]) for i in order])
+                res[f"ceiling_{pname}_GBps"] = round(nbytes / t / 1e6, 1)
+                res[f"{pname}_frac_of_ceiling"] = round(res[f"{pname}_GBps"] / (nbytes / t / 1e6), 4)
+            del fsets
+        res.update({"bwd": "in place" if w.in_place else "out of place", "buffer_sets": sets,
+                    "timing": f"HIP graph of {len(order)} launches cycling over the buffer sets, "
+                              f"median of {replays} replays"})
+        out[w.name] = res
+        samples[w.name] = sample
+    return out, samples
+
+
+def ceiling_leg(dev, stream, w, x, dy, y, dx, fwd_ms: float, bwd_ms: float, batches: int = 10,
+                per_batch: int = 5):
+    """Zero-arithmetic streaming ceilings at the headline size: the row-packed
+    patterns on the workload's own buffers, and every independent structure
+    (ceiling.STRUCTURES) on separate flat streams of the same bytes, for the
+    forward and backward mixes and for read-only, write-only and copy
+    traffic. Median over `batches` batches of `per_batch` back-to-back
+    launches. The SwiGLU kernels' times are set against the best of all."""
+    import numpy as np
+    import torch
+
+    import ceiling
+    e = w.elem_bytes
+    nv16 = w.n * e // 16
+    nvec = w.rows * nv16
+
+    def timed(fn):
+        fn()
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(batches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(per_batch):
+                fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) / per_batch)
+        return float(np.median(ts))
+
+    res = {"row_packed": {}, "independent": {}}
+    for pattern, mix, out in ((0, "fwd", y), (1, "bwd", dx)):
+        t = timed(lambda: ceiling.launch(pattern, x, dy, out, w.rows, nv16, stream))
+        res["row_packed"][mix] = {"ms": round(t, 5),
+                                  "GBps": round(ceiling.mix_bytes(mix, nvec) / t / 1e6, 1)}
+    fs = ceiling.FlatStreams(nvec, dev)
+    for mix in ceiling.MIXES:
+        res["independent"][mix] = {}
+        for s, sname in ceiling.STRUCTURES.items():
+            t = timed(lambda: ceiling.probe(s, mix, fs, stream))
+            res["independent"][mix][sname] = round(ceiling.mix_bytes(mix, nvec) / t / 1e6, 1)
+    del fs
+    best = {}
+    for mix, kernel_ms in (("fwd", fwd_ms), ("bwd", bwd_ms)):
+        cands = dict(res["independent"][mix])
+        cands["row-packed (the SwiGLU kernels' structure)"] = res["row_packed"][mix]["GBps"]
+        sname = max(cands, key=cands.get)
+        kernel_gbps = ceiling.mix_bytes(mix, nvec) / kernel_ms / 1e6
+        ind = max(res["independent"][mix], key=res["independent"][mix].get)
+        best[mix] = {"best_structure": sname, "GBps": cands[sname],
+                     "best_independent_structure": ind,
+                     "best_independent_GBps": res["independent"][mix][ind],
+                     "kernel_GBps": round(kernel_gbps, 1),
+                     "kernel_frac_of_best": round(kernel_gbps / cands[sname], 4)}
+    res["best"] = best
+    return res
+
+
+def oracle_parity(dtype: str, got, ref, den=None) -> dict:
+    """Stored GPU outputs (float32 values, or bf16 bit patterns) against
+    float64 oracle values: bf16 by ulp distance to the correctly rounded value
+    (bar 2), fp32 by relative error (bar 1e-5; where the reference is 0 the
+    output must be 0). den: for dgate, the scale |dy u sigma| (1 + |g| (1 -
+    sigma)) of the scale-aware error, reported beside the bar, not gated."""
+    import numpy as np
+
+    import oracle
+    st = {"elements": int(ref.size)}
+    if dtype == "bf16":
+        d = oracle.bf16_ulp_distance(got, oracle.round_f64_to_bf16_bits(ref))
+        st.update({"max_ulp": int(d.max()) if d.size else 0,
+                   "over_2_ulp": int(np.count_nonzero(d > 2))})
+        g = oracle.bf16_bits_to_f64(got)
+    else:
+        g = np.asarray(got, dtype=np.float64)
+        nz = ref != 0
+        rel = np.abs(g - ref)[nz] / np.abs(ref[nz])
+        st.update({"max_rel": float(rel.max()) if rel.size else 0.0,
+                   "over_1e-5": int(np.count_nonzero(rel > 1e-5)) +
+                   int(np.count_nonzero((~nz) & (g != 0)))})
+    if den is not None:
+        m = den > 0
+        st["max_scale_aware"] = float((np.abs(g - ref)[m] / den[m]).max()) if m.any() else 0.0
+    return st
+
+
+def oracle_parity_of_sample(dtype: str, n: int, s: dict) -> dict:
+    """Per-pass parity of one sample of timed outputs (configs leg)."""
+    import numpy as np
+
+    import oracle
+    xf, dyf = oracle.widen(s["x"], dtype), oracle.widen(s["dy"], dtype)
+    y_ref, dx_ref = oracle.oracle_fwd(xf), oracle.oracle_bwd(xf, dyf)
+    g, u = xf[:, :n], xf[:, n:]
+    sig = oracle.sigmoid(g)
+    den = np.abs(dyf * u * sig) * (1.0 + np.abs(g) * (1.0 - sig))
+    return {"rows": s["rows"],
+            "fwd": oracle_parity(dtype, s["y"], y_ref),
+            "bwd_dgate": oracle_parity(dtype, s["dx"][:, :n], dx_ref[:, :n], den),
+            "bwd_dup": oracle_parity(dtype, s["dx"][:, n:], dx_ref[:, n:])}
+
+
+def calib_copies(dev):
+    """Known-size plain copies, each reading and writing exactly CALIB_BYTES
+    (torch copy_ and an elementwise negation): the byte-counter calibration
+    for rocprofv3 --pmc runs."""
+    import torch
+    src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"[bench] calibration copies of {CALIB_BYTES} bytes done")
 
 
 def main():
@@ -412,6 +592,10 @@ def main():
     ap.add_argument("--bias-scale-only", action="store_true",
                     help="time only the bias / per-token-scale forward and backward on the "
                          "workload, print their figures as one JSON line, and exit")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="time only the other workloads' forward and backward (rotated buffers, "
+                         "graph replay): the one named by --workload, else all but the headline; "
+                         "print their figures as one JSON line, and exit (for profiling runs)")
     ap.add_argument("--calib", action="store_true",
                     help="also run plain 1 GiB copies (torch copy_ and an elementwise "
                          "negation) as the byte-counter calibration for rocprofv3 --pmc")
@@ -443,6 +627,13 @@ def main():
     if args.fc1_only:
         res = fc1_leg(dev, torch.cuda.current_stream(dev), w.rows, iters=args.steps)
         print(json.dumps({"fc1_swiglu": res}), flush=True)
+        return
+    if args.configs_only:
+        names = [args.workload] if args.workload else [k for k in synth.WORKLOADS if k != synth.HEADLINE]
+        res, _ = configs_leg(dev, torch.cuda.current_stream(dev), names)
+        if args.calib:
+            calib_copies(dev)
+        print(json.dumps({"other_workloads": res}), flush=True)
         return
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     log(f"[bench] workload {w.name}: x {w.shape} {w.dtype}; drawing inputs")
@@ -507,9 +698,11 @@ def main():
         timed_outputs = (stored(y, w.n), stored(dx, 2 * w.n))
 
     passes = {
-        "fwd": {"ms_avg": round(fwd_avg, 5), "ms_min": round(min(fwd_ms), 5),
+        "fwd": {"ms_avg": round(fwd_avg, 5), "ms_median": round(float(np.median(fwd_ms)), 5),
+                "ms_min": round(min(fwd_ms), 5), "ms_max": round(max(fwd_ms), 5),
                 "GBps": round(fwd_bytes / fwd_avg / 1e6, 1), "bytes": fwd_bytes},
-        "bwd": {"ms_avg": round(bwd_avg, 5), "ms_min": round(min(bwd_ms), 5),
+        "bwd": {"ms_avg": round(bwd_avg, 5), "ms_median": round(float(np.median(bwd_ms)), 5),
+                "ms_min": round(min(bwd_ms), 5), "ms_max": round(max(bwd_ms), 5),
                 "GBps": round(bwd_bytes / bwd_avg / 1e6, 1), "bytes": bwd_bytes},
         "fwd+bwd_kernels": {"ms_avg": round(fwd_avg + bwd_avg, 5),
                             "GBps": round(step_bytes / (fwd_avg + bwd_avg) / 1e6, 1)},
@@ -590,47 +783,22 @@ def main():
         passes["bias_scale"] = bias_scale_leg(dev, stream, w, x, dy, y, dx)
         log(f"[bench] bias+scale fwd {passes['bias_scale']['fwd_ms']:.4f} ms, "
             f"bwd {passes['bias_scale']['bwd_ms']:.4f} ms")
-        passes["other_workloads"] = configs_leg(dev, stream, w.name)
+        passes["other_workloads"], config_samples = configs_leg(
+            dev, stream, [k for k in synth.WORKLOADS if k != w.name])
         log("[bench] other workloads: " + ", ".join(
             f"{k} fwd {v['fwd_GBps']:.0f} bwd {v['bwd_GBps']:.0f} GB/s"
             for k, v in passes["other_workloads"].items()))
         passes["fc1_swiglu"] = fc1_leg(dev, stream, w.rows)
         if (w.n * e) % 16 == 0 and w.rows <= 65535:
-            # The same access patterns with no arithmetic: the best this memory
-            # system streams for each mix, on the same buffers and grid.
-            import ceiling
-            nv16 = w.n * e // 16
-
-            def ceil_ms(pattern, out):
-                ts = []
-                for k in range(22):
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    ceiling.launch(pattern, x, dy, out, w.rows, nv16, stream)
-                    b.record(stream)
-                    b.synchronize()
-                    if k >= 2:
-                        ts.append(a.elapsed_time(b))
-                return float(np.mean(ts))
-
-            c0, c1 = ceil_ms(0, y), ceil_ms(1, dx)
-            passes["ceiling_fwd_mix"] = {"ms_avg": round(c0, 5), "GBps": round(fwd_bytes / c0 / 1e6, 1),
-                                         "fwd_frac_of_ceiling": round(c0 / fwd_avg, 4)}
-            passes["ceiling_bwd_mix"] = {"ms_avg": round(c1, 5), "GBps": round(bwd_bytes / c1 / 1e6, 1),
-                                         "bwd_frac_of_ceiling": round(c1 / bwd_avg, 4)}
-            log(f"[bench] ceiling: fwd mix {c0:.4f} ms, bwd mix {c1:.4f} ms")
+            passes["ceiling"] = ceiling_leg(dev, stream, w, x, dy, y, dx, fwd_avg, bwd_avg)
+            cb = passes["ceiling"]["best"]
+            log(f"[bench] ceiling: fwd mix best {cb['fwd']['GBps']:.0f} GB/s "
+                f"({cb['fwd']['best_structure']}), bwd mix best {cb['bwd']['GBps']:.0f} GB/s "
+                f"({cb['bwd']['best_structure']}); independent best fwd "
+                f"{cb['fwd']['best_independent_GBps']:.0f}, bwd {cb['bwd']['best_independent_GBps']:.0f}")
 
     if args.calib:
-        # Known-size plain copies: each reads and writes exactly CALIB_BYTES.
-        src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"[bench] calibration copies of {CALIB_BYTES} bytes done")
+        calib_copies(dev)
 
     achieved = bwd_bytes / (bwd_avg * 1e-3) / 1e9
     traffic = read_traffic()
@@ -662,6 +830,12 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for about {args.cpu_seconds} s")
         out["cpu_baseline"] = cpu_baseline(w, x_h, dy_h, args.cpu_seconds, timed_outputs)
+        if not args.no_extras:
+            # the oracle against sampled rows of every other workload's timed outputs
+            for name, smp in config_samples.items():
+                wk = synth.WORKLOADS[name]
+                passes["other_workloads"][name]["parity"] = oracle_parity_of_sample(wk.dtype, wk.n, smp)
+            del config_samples
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -1,10 +1,28 @@
-// Empirical streaming ceiling for the SwiGLU access patterns (measurement only,
-// not part of the SwiGLU path). Same grid, lane mapping, 16-byte vectors and
-// nontemporal hints as the wide SwiGLU kernels, with the arithmetic replaced by
-// an XOR, so the time is what the memory system allows for that mix:
-//   pattern 0 (forward mix):  read two half rows of x, write one row of y;
-//   pattern 1 (backward mix): read two half rows of x and one row of dy,
-//                             write two half rows of dx.
+// Empirical streaming ceilings for the SwiGLU access patterns (measurement
+// only, not part of the SwiGLU path). Every kernel here moves the bytes of a
+// traffic mix with the arithmetic replaced by an XOR, so its time is what the
+// memory system allows for that mix under that kernel structure.
+//
+// Two families:
+//  * Row-packed (stream_ceiling_launch): the same grid, lane mapping, 16-byte
+//    vectors and nontemporal hints as the wide SwiGLU kernels. It shows how
+//    much of the SwiGLU kernels' time the arithmetic adds.
+//      pattern 0 (forward mix):  read two half rows of x, write one row of y;
+//      pattern 1 (backward mix): read two half rows of x and one row of dy,
+//                                write two half rows of dx.
+//  * Independent structures (stream_probe_launch) over separate flat streams
+//    of 16-byte vectors, built differently from the SwiGLU kernels, so that
+//    the best of them is a ceiling the SwiGLU kernels' design does not set:
+//      structure 0: one-shot grid, 256 lanes per block, one vector per lane;
+//      structure 1: one-shot grid, 1024 lanes per block, one vector per lane;
+//      structure 2: persistent grid-stride loop, 256 lanes, 8 blocks per CU,
+//                   4 vectors per lane and stream in flight per iteration;
+//      structure 3: block-contiguous chunks, 256 lanes, 4 blocks per CU, each
+//                   block walking its own contiguous range 2 vectors per lane
+//                   at a time;
+//    and mixes 0 forward (r0, r1 -> w0), 1 backward (r0, r1, r2 -> w0, w1),
+//    2 read-only (r0), 3 write-only (w0), 4 copy (r0 -> w0). Structures 0-2
+//    take the nontemporal hint on every access; `cached` drops it.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -13,16 +31,25 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ u32x4 ld(const u32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void st(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st(u32x4* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
+// ---- row-packed (the SwiGLU kernels' structure) -----------------------------
 // nv: 16-byte vectors per half row; x rows are 2*nv vectors, y/dy rows nv.
 __global__ __launch_bounds__(256) void mix_2r1w(const u32x4* x, u32x4* y, uint32_t nv) {
     const uint32_t c = blockIdx.x * 256u + threadIdx.x;
     if (c >= nv) return;
     const size_t r = blockIdx.y;
     const u32x4* xr = x + r * 2 * nv + c;
-    st(y + r * nv + c, ld(xr) ^ ld(xr + nv));
+    st<true>(y + r * nv + c, ld<true>(xr) ^ ld<true>(xr + nv));
 }
 
 __global__ __launch_bounds__(256) void mix_3r2w(const u32x4* dy, const u32x4* x, u32x4* dx,
@@ -31,18 +58,112 @@ __global__ __launch_bounds__(256) void mix_3r2w(const u32x4* dy, const u32x4* x,
     if (c >= nv) return;
     const size_t r = blockIdx.y;
     const u32x4* xr = x + r * 2 * nv + c;
-    const u32x4 a = ld(xr), b = ld(xr + nv), d = ld(dy + r * nv + c);
+    const u32x4 a = ld<true>(xr), b = ld<true>(xr + nv), d = ld<true>(dy + r * nv + c);
     u32x4* o = dx + r * 2 * nv + c;
-    st(o, a ^ d);
-    st(o + nv, b ^ d);
+    st<true>(o, a ^ d);
+    st<true>(o + nv, b ^ d);
+}
+
+// ---- independent structures over flat streams --------------------------------
+// Vectors [lo, hi) are visited in groups of BS*U: lane t of the group starting
+// at `base` takes base + u*BS + t for u < U. Grid-stride mode (chunk == 0):
+// block b starts at b*BS*U and steps by gridDim.x*BS*U. Chunk mode: block b
+// owns [b*chunk, (b+1)*chunk) and steps by BS*U.
+template <int MIX, int U, int BS, bool NT>
+__global__ __launch_bounds__(BS) void flat_kernel(const u32x4* __restrict__ r0,
+                                                  const u32x4* __restrict__ r1,
+                                                  const u32x4* __restrict__ r2,
+                                                  u32x4* __restrict__ w0, u32x4* __restrict__ w1,
+                                                  uint64_t nvec, uint64_t chunk) {
+    uint64_t lo, hi, step;
+    if (chunk == 0) {
+        lo = (uint64_t)blockIdx.x * BS * U;
+        hi = nvec;
+        step = (uint64_t)gridDim.x * BS * U;
+    } else {
+        lo = (uint64_t)blockIdx.x * chunk;
+        hi = lo + chunk < nvec ? lo + chunk : nvec;
+        step = (uint64_t)BS * U;
+    }
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (uint64_t base = lo; base < hi; base += step) {
+        u32x4 a[U], b[U], c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t i = base + (uint64_t)u * BS + threadIdx.x;
+            if (i < hi) {
+                if constexpr (MIX != 3) a[u] = ld<NT>(r0 + i);
+                if constexpr (MIX <= 1) b[u] = ld<NT>(r1 + i);
+                if constexpr (MIX == 1) c[u] = ld<NT>(r2 + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t i = base + (uint64_t)u * BS + threadIdx.x;
+            if (i < hi) {
+                if constexpr (MIX == 0) st<NT>(w0 + i, a[u] ^ b[u]);
+                if constexpr (MIX == 1) {
+                    st<NT>(w0 + i, a[u] ^ c[u]);
+                    st<NT>(w1 + i, b[u] ^ c[u]);
+                }
+                if constexpr (MIX == 2) acc ^= a[u];
+                if constexpr (MIX == 3) {
+                    const u32x4 v = {(uint32_t)i, 1u, 2u, 3u};
+                    st<NT>(w0 + i, v);
+                }
+                if constexpr (MIX == 4) st<NT>(w0 + i, a[u]);
+            }
+        }
+    }
+    if constexpr (MIX == 2) {
+        // keeps the loads alive; true only for a pattern the callers never store
+        if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x01234567u &&
+            acc.w == 0x89abcdefu && w0 != nullptr) {
+            const uint64_t i = (uint64_t)blockIdx.x * BS + threadIdx.x;
+            if (i < nvec) w0[i] = acc;
+        }
+    }
+}
+
+template <int MIX, int U, int BS, bool NT>
+hipError_t flat_launch(uint32_t grid, const u32x4* r0, const u32x4* r1, const u32x4* r2, u32x4* w0,
+                       u32x4* w1, uint64_t nvec, uint64_t chunk, hipStream_t s) {
+    hipLaunchKernelGGL((flat_kernel<MIX, U, BS, NT>), dim3(grid), dim3(BS), 0, s, r0, r1, r2, w0,
+                       w1, nvec, chunk);
+    return hipGetLastError();
+}
+
+template <int MIX, bool NT>
+hipError_t structure_launch(int structure, int cus, const u32x4* r0, const u32x4* r1,
+                            const u32x4* r2, u32x4* w0, u32x4* w1, uint64_t nvec, hipStream_t s) {
+    auto groups = [&](uint64_t per) { return (nvec + per - 1) / per; };
+    switch (structure) {
+        case 0:
+            return flat_launch<MIX, 1, 256, NT>((uint32_t)groups(256), r0, r1, r2, w0, w1, nvec, 0, s);
+        case 1:
+            return flat_launch<MIX, 1, 1024, NT>((uint32_t)groups(1024), r0, r1, r2, w0, w1, nvec, 0, s);
+        case 2: {
+            uint64_t g = groups(1024);
+            if (g > (uint64_t)cus * 8) g = (uint64_t)cus * 8;
+            return flat_launch<MIX, 4, 256, NT>((uint32_t)g, r0, r1, r2, w0, w1, nvec, 0, s);
+        }
+        case 3: {
+            uint64_t g = (uint64_t)cus * 4;
+            uint64_t chunk = (groups(g) + 511) / 512 * 512;     // whole groups of 256 x 2
+            g = groups(chunk);
+            return flat_launch<MIX, 2, 256, NT>((uint32_t)g, r0, r1, r2, w0, w1, nvec, chunk, s);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 extern "C" {
 
-// Returns 0 on a successful launch, -1 on bad arguments, 1 on a launch error.
-// rows <= 65535 (one launch); buffers must hold the extents described above.
+// Row-packed patterns. Returns 0 on a successful launch, -1 on bad arguments,
+// 1 on a launch error. rows <= 65535 (one launch); x holds rows * 2nv vectors,
+// y (pattern 0) rows * nv, dy rows * nv and dx (pattern 1) rows * 2nv.
 __attribute__((visibility("default"))) int stream_ceiling_launch(
     int pattern, const void* x, const void* dy, void* out, int64_t rows, int64_t nv,
     hipStream_t stream) {
@@ -61,6 +182,48 @@ __attribute__((visibility("default"))) int stream_ceiling_launch(
         return -1;
     }
     return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// Independent structures over flat streams of nvec 16-byte vectors each. The
+// streams a mix uses must be non-NULL, 16-byte aligned and hold nvec vectors:
+// forward r0, r1, w0; backward r0, r1, r2, w0, w1; read-only r0 (and w0, which
+// is never written for the data the callers use); write-only w0; copy r0, w0.
+// Returns 0 on a successful launch, -1 on bad arguments, 1 on a launch error.
+__attribute__((visibility("default"))) int stream_probe_launch(
+    int structure, int mix, int cached, const void* r0, const void* r1, const void* r2, void* w0,
+    void* w1, int64_t nvec, hipStream_t stream) {
+    if (nvec <= 0 || nvec > ((int64_t)1 << 40) || structure < 0 || structure > 3 || mix < 0 ||
+        mix > 4)
+        return -1;
+    const bool need_r0 = mix != 3, need_r1 = mix <= 1, need_r2 = mix == 1;
+    const bool need_w0 = true, need_w1 = mix == 1;
+    if ((need_r0 && !r0) || (need_r1 && !r1) || (need_r2 && !r2) || (need_w0 && !w0) ||
+        (need_w1 && !w1))
+        return -1;
+    if (((uintptr_t)r0 | (uintptr_t)r1 | (uintptr_t)r2 | (uintptr_t)w0 | (uintptr_t)w1) % 16)
+        return -1;
+    if ((nvec + 255) / 256 > (int64_t)UINT32_MAX) return -1;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 1;
+    const u32x4 *a = (const u32x4*)r0, *b = (const u32x4*)r1, *c = (const u32x4*)r2;
+    u32x4 *o0 = (u32x4*)w0, *o1 = (u32x4*)w1;
+    const uint64_t nv = (uint64_t)nvec;
+    hipError_t e = hipErrorInvalidValue;
+#define SWIGLU_CEIL_MIX(M)                                                                   \
+    e = cached ? structure_launch<M, false>(structure, cus, a, b, c, o0, o1, nv, stream)   \
+               : structure_launch<M, true>(structure, cus, a, b, c, o0, o1, nv, stream);   \
+    break;
+    switch (mix) {
+        case 0: SWIGLU_CEIL_MIX(0)
+        case 1: SWIGLU_CEIL_MIX(1)
+        case 2: SWIGLU_CEIL_MIX(2)
+        case 3: SWIGLU_CEIL_MIX(3)
+        case 4: SWIGLU_CEIL_MIX(4)
+    }
+#undef SWIGLU_CEIL_MIX
+    return e == hipSuccess ? 0 : 1;
 }
 
 }  // extern "C"

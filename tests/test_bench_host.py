@@ -91,3 +91,45 @@ def test_cpu_baseline_compares_the_timed_outputs_with_the_oracle():
     assert r["max_ulp_fwd"] == 0 and r["max_ulp_bwd"] == 3 and r["over_2_ulp"] == 1
     # without outputs there is no comparison
     assert bench.cpu_baseline(w, x, dy, seconds=30.0)["timed_outputs_vs_oracle"] is None
+
+
+def test_oracle_parity_counts_planted_errors():
+    import oracle
+    rng = np.random.default_rng(1)
+    ref = rng.standard_normal(1000)
+    # bf16: the correctly rounded bits, one element moved 3 steps and one 2
+    bits = oracle.round_f64_to_bf16_bits(ref).copy()
+    bits[10] += 3
+    bits[20] += 2
+    st = bench.oracle_parity("bf16", bits, ref)
+    assert st == {"elements": 1000, "max_ulp": 3, "over_2_ulp": 1}
+    # fp32: one element 2e-5 off in relative terms, one nonzero where ref is 0
+    ref[5] = 0.0
+    got = ref.astype(np.float32)
+    got[7] = np.float32(ref[7] * (1 + 2e-5))
+    got[5] = np.float32(1e-30)
+    st = bench.oracle_parity("fp32", got, ref, den=np.abs(ref) + 1.0)
+    assert st["over_1e-5"] == 2
+    assert 1.5e-5 < st["max_rel"] < 2.5e-5
+    assert st["max_scale_aware"] > 0
+
+
+def test_oracle_parity_of_exact_sample_is_clean():
+    import oracle
+    import synth
+    for name in ("tiny_fp32_s16_b4_n128", "inplace_tp_bf16_t8192_n1792"):
+        w = synth.WORKLOADS[name]
+        x, dy = synth.make_x(w, 0, 16), synth.make_dy(w, 0, 16)
+        xf, dyf = oracle.widen(x, w.dtype), oracle.widen(dy, w.dtype)
+        y, dx = oracle.oracle_fwd(xf), oracle.oracle_bwd(xf, dyf)
+        if w.dtype == "bf16":
+            y, dx = oracle.round_f64_to_bf16_bits(y), oracle.round_f64_to_bf16_bits(dx)
+        else:
+            y, dx = y.astype(np.float32), dx.astype(np.float32)
+        st = bench.oracle_parity_of_sample(w.dtype, w.n, {"rows": [0, 16], "x": x, "dy": dy,
+                                                          "y": y, "dx": dx})
+        key = "over_2_ulp" if w.dtype == "bf16" else "over_1e-5"
+        for p in ("fwd", "bwd_dgate", "bwd_dup"):
+            assert st[p][key] == 0 and st[p]["elements"] == 16 * w.n
+        # storage rounding alone: half a step of the stored type, relative
+        assert st["bwd_dgate"]["max_scale_aware"] < (2.0 ** -8 if w.dtype == "bf16" else 1e-6)
