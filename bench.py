@@ -192,14 +192,24 @@ def cpu_baseline_other_rows(w, x_h, dy_h, rows: int = 512):
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 
 
-def pair_times(stream, f1, f2, iters: int, warm: int = 2):
-    """Mean event times (ms) of f1 and of f2, run alternately iters + warm
-    times back to back on `stream`, the first `warm` pairs discarded. One
-    synchronisation at the end, so the GPU never idles between launches."""
+def pair_times(stream, f1, f2, iters: int, warm_s: float = 0.1):
+    """Median event times (ms) of f1 and of f2, run alternately back to back
+    on `stream`: untimed pairs for `warm_s` seconds first (the first few
+    milliseconds of a new load can run up to 15 % slow while the clocks
+    settle), then `iters` timed pairs with one synchronisation at the end, so
+    the GPU never idles between launches."""
     import numpy as np
     import torch
+    t_end = time.perf_counter() + warm_s
+    while True:
+        for _ in range(4):
+            f1()
+            f2()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
     ev = []
-    for _ in range(iters + warm):
+    for _ in range(iters):
         a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record(stream)
         f1()
@@ -208,8 +218,8 @@ def pair_times(stream, f1, f2, iters: int, warm: int = 2):
         c.record(stream)
         ev.append((a, b, c))
     ev[-1][2].synchronize()
-    t = [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev[warm:]]
-    return float(np.mean([x[0] for x in t])), float(np.mean([x[1] for x in t]))
+    t = [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev]
+    return float(np.median([x[0] for x in t])), float(np.median([x[1] for x in t]))
 
 
 def hbm_roofline(kernel: str, bytes_: float, ms: float) -> dict:
@@ -281,7 +291,7 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
     return out
 
 
-def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
+def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 20):
     """Bias + per-token scale variants on the workload's tensors: forward,
     and backward with dx, dbias and dscale (the reductions included)."""
     import torch
@@ -308,7 +318,7 @@ def bias_scale_leg(dev, stream, w, x, dy, y, dx, iters: int = 10):
     fwd_alg, bwd_alg = fwd_bytes + extra_in, bwd_bytes + extra_in + 4 * 2 * w.n + 4 * w.rows
     return {"fwd_ms": round(bf, 5), "bwd_ms": round(bb, 5),
             "roofline_fwd": hbm_roofline("swiglu_fwd_bs_kernel (bias, scale)", fwd_alg, bf),
-            "roofline_bwd": hbm_roofline("swiglu_bwd_bs_kernel + sums (dx, dbias, dscale)",
+            "roofline_bwd": hbm_roofline("swiglu_bwd_bs_tile_kernel + sums (dx, dbias, dscale)",
                                          bwd_alg, bb),
             "fwd_GBps": round(fwd_bytes / bf / 1e6, 1),
             "bwd_GBps": round(bwd_bytes / bb / 1e6, 1),
@@ -651,6 +661,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.bias_scale_only:
         res = bias_scale_leg(dev, stream, w, x, dy, y, dx, iters=args.steps)
+        if args.calib:
+            calib_copies(dev)
         print(json.dumps({"bias_scale": res}), flush=True)
         return
 

@@ -255,7 +255,7 @@ swiglu_status swiglu_gateup_bias_scale_bwd(const void* dy, int64_t dy_row_stride
  *   Limit: swiglu_gateup_bias_scale_workspace_size(rows, n, dbias != NULL,
  *   dscale != NULL) must not exceed SWIGLU_NOALLOC_SCRATCH_BYTES; larger
  *   problems return SWIGLU_ERR_SCRATCH_LIMIT before anything is launched.
- *   (8192 rows of n = 32768 with both sums need 32 MiB.)
+ *   (8192 rows of n = 32768 with both sums need 48 MiB.)
  *   Concurrency: every call on one GPU shares that GPU's array, so calls on
  *   one GPU that may overlap in time (different streams, or different host
  *   threads without ordering) race and must not be issued. The array needs

@@ -33,11 +33,33 @@ using namespace swiglu_impl;
 #ifndef SWIGLU_BS_ONE_SHOT
 #define SWIGLU_BS_ONE_SHOT 1           // backward without dbias on wide rows: one-shot grid
 #endif
+#ifndef SWIGLU_BS_TILE
+#define SWIGLU_BS_TILE 1               // backward with dbias on wide rows: one-shot tile kernel
+#endif
+#ifndef SWIGLU_BS_TILE_WAVES
+#define SWIGLU_BS_TILE_WAVES 16        // waves per tile block, each on its own rows
+#endif
+#ifndef SWIGLU_BS_TILE_RPL
+#define SWIGLU_BS_TILE_RPL 2           // rows per lane and phase in the tile kernel
+#endif
+#ifndef SWIGLU_BS_TILE_PHASES
+#define SWIGLU_BS_TILE_PHASES 2        // phases of the tile kernel (rows per lane = RPL x PHASES)
+#endif
+#ifndef SWIGLU_BS_TILE_MIN_BLOCKS
+#define SWIGLU_BS_TILE_MIN_BLOCKS 1    // tile blocks per CU the register budget must allow
+#endif
 #ifndef SWIGLU_BS_INTERLEAVE
 #define SWIGLU_BS_INTERLEAVE 1         // group y takes rows y, y+G, y+2G, ... (else a band)
 #endif
 constexpr int kBsRows = SWIGLU_BS_ROWS_PER_GROUP;
 constexpr int kWaves = kBlock / 64;
+constexpr int kTileWaves = SWIGLU_BS_TILE_WAVES;
+constexpr int kTileRpl = SWIGLU_BS_TILE_RPL;
+constexpr int kTilePhases = SWIGLU_BS_TILE_PHASES;
+constexpr int kTileRows = kTileWaves * kTileRpl * kTilePhases;   // rows per tile block (one partial)
+constexpr int kTileThreads = 64 * kTileWaves;
+// Rows per dbias partial, at most: the workspace is sized for the smaller group.
+constexpr int kMinGroupRows = kTileRows < kBsRows ? kTileRows : kBsRows;
 
 // Exact sum of two fp32 values as head + tail (Knuth's two-sum).
 __device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
@@ -194,7 +216,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // One element of the backward: z = x + bias (the gate carried as a two-sum,
 // so the root series sees the sum's rounding error), dz for gate and up, and
 // the element's term dy * silu(z_g) * z_u added to p (for dscale). Shared by
-// the row-loop and one-shot kernels so that both give the same bits.
+// the row-loop, tile and one-shot kernels so that all give the same bits.
 template <typename T>
 __device__ __forceinline__ void bwd_bs_elem(float g, float u, float d, float bg, float bu, float s,
                                             float& dg, float& du, float& p) {
@@ -469,26 +491,142 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_bs1_kernel(
     }
 }
 
-// out[k * out_stride] = sum over j < count of part[j * jstride + k * kstride],
-// j in order, for k < width.
-__global__ __launch_bounds__(kBlock) void swiglu_sum_partials_kernel(
-    const float* __restrict__ part, int64_t count, int64_t jstride, int64_t kstride,
-    int64_t width, float* __restrict__ out, int64_t out_stride) {
-    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (k >= width) return;
-    const float* p = part + k * kstride;
+// The backward with dbias on wide rows of 16-byte vectors, as a one-shot
+// grid. Block (x, y) owns vectors [64 x, 64 x + 64) of the kTileRows rows
+// [y R, (y + 1) R), R = W * kTileRpl * kTilePhases with W = kTileWaves: wave
+// w takes rows y R + k W + w for k < kTileRpl * kTilePhases, each wave on its
+// own rows. The rows come in kTilePhases phases of kTileRpl rows, and every
+// lane issues all loads of a phase before the first is used. Each lane adds
+// its rows' dz in row order; the waves' sums then go through LDS and are
+// added in wave order, one thread per column, into this block's dbias
+// partial part_db[group][k], written with consecutive threads on
+// consecutive columns. The dscale partial of each (row, 64-vector chunk) is
+// the chunk's wave sum, stored where the row-loop kernel stores it (chunk x
+// of this grid is wave x % 4 of the row loop's tile x / 4), so dscale is the
+// same bits either way. Fixed summation order throughout.
+template <typename T, int VEC, bool IN_PLACE, bool HAS_BIAS, bool HAS_SCALE, bool WANT_DS>
+__global__ __launch_bounds__(kTileThreads, SWIGLU_BS_TILE_MIN_BLOCKS) void swiglu_bwd_bs_tile_kernel(
+    const T* dyp, int64_t dys, T* gp, int64_t gs, T* up, int64_t us, T* dgp, int64_t dgs,
+    T* dup, int64_t dus, const T* __restrict__ bg, const T* __restrict__ bu,
+    const float* __restrict__ sc, int64_t scs, float* part_db, float* part_ds, BsGeom G) {
+    if constexpr (IN_PLACE) {
+        dgp = gp;
+        dgs = gs;
+        dup = up;
+        dus = us;
+    }
+    constexpr int kVals = 2 * VEC;                      // dz values per lane and row
+    constexpr int kPad = kVals + 1;                     // LDS words per lane (odd: no conflicts)
+    __shared__ float lds[kTileWaves * 64 * kPad];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t col = blockIdx.x * 64u + (uint32_t)lane;
+    const bool active = col < G.nv;
+    const int64_t c = (int64_t)col * VEC;
+    const int64_t rbase = (int64_t)blockIdx.y * kTileRows + wave;
+    typedef typename Vec<T, VEC>::R R;
+    R bgr{}, bur{};
+    if (HAS_BIAS && active) {
+        bgr = *reinterpret_cast<const R*>(bg + c);      // re-read by every row: cached
+        bur = *reinterpret_cast<const R*>(bu + c);
+    }
+    float acc[kVals];
+#pragma unroll
+    for (int i = 0; i < kVals; ++i) acc[i] = 0.0f;
+    for (int ph = 0; ph < kTilePhases; ++ph) {
+        R gr[kTileRpl], ur[kTileRpl], dr[kTileRpl];
+        float s[kTileRpl];
+#pragma unroll
+        for (int k = 0; k < kTileRpl; ++k) {
+            const int64_t row = rbase + (int64_t)(ph * kTileRpl + k) * kTileWaves;
+            gr[k] = ur[k] = dr[k] = R{};
+            if (active && row < G.rows) {
+                gr[k] = load_raw<R>(gp + row * gs + c);
+                ur[k] = load_raw<R>(up + row * us + c);
+                dr[k] = load_raw<R>(dyp + row * dys + c);
+            }
+            s[k] = HAS_SCALE && row < G.rows ? sc[row * scs] : 1.0f;
+        }
+        float b[VEC], e[VEC];
+        widen_bits<T, VEC>(bgr, b);                     // zero bits when there is no bias
+        widen_bits<T, VEC>(bur, e);
+#pragma unroll
+        for (int k = 0; k < kTileRpl; ++k) {
+            const int64_t row = rbase + (int64_t)(ph * kTileRpl + k) * kTileWaves;
+            if (row >= G.rows) break;                   // uniform
+            float p = 0.0f;
+            if (active) {
+                float g[VEC], u[VEC], d[VEC], dg[VEC], du[VEC];
+                widen_bits<T, VEC>(gr[k], g);
+                widen_bits<T, VEC>(ur[k], u);
+                widen_bits<T, VEC>(dr[k], d);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    bwd_bs_elem<T>(g[i], u[i], d[i], b[i], e[i], s[k], dg[i], du[i], p);
+                    acc[i] += dg[i];
+                    acc[VEC + i] += du[i];
+                }
+                Vec<T, VEC>::store(dgp + row * dgs + c, dg);
+                Vec<T, VEC>::store(dup + row * dus + c, du);
+            }
+            if constexpr (WANT_DS) {
+                const float w = wave_sum(p);
+                if (lane == 0) part_ds[(int64_t)blockIdx.x * G.total_rows + G.row0 + row] = w;
+            }
+        }
+    }
+    float* mine = lds + (wave * 64 + lane) * kPad;
+#pragma unroll
+    for (int i = 0; i < kVals; ++i) mine[i] = acc[i];
+    __syncthreads();
+    // thread t: column k = t % (64 VEC) of half t / (64 VEC) of this block
+    for (int t = threadIdx.x; t < 64 * kVals; t += kTileThreads) {
+        const int half = t / (64 * VEC), k = t % (64 * VEC);
+        const int l = k / VEC, j = k % VEC;
+        if (blockIdx.x * 64u + (uint32_t)l < G.nv) {
+            const float* src = lds + l * kPad + half * VEC + j;
+            float sum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kTileWaves; ++w) sum += src[w * 64 * kPad];
+            part_db[(G.group0 + blockIdx.y) * (2 * G.n) + half * G.n +
+                    (int64_t)blockIdx.x * 64 * VEC + k] = sum;
+        }
+    }
+}
+
+// One fixed-order column of partial sums: out[k * out_stride] = sum over
+// j < count of part[j * jstride + k * kstride], j in order.
+struct PartialSum {
+    const float* part;
+    int64_t count, jstride, kstride, width;
+    float* out;
+    int64_t out_stride;
+    int64_t blocks;     // blocks of kBlock threads over width
+};
+
+__device__ __forceinline__ void sum_one(const PartialSum& S, int64_t k) {
+    if (k >= S.width) return;
+    const float* p = S.part + k * S.kstride;
     float acc = 0.0f;
     int64_t j = 0;
-    // eight loads in flight, added in the same order as the plain loop
-    for (; j + 8 <= count; j += 8) {
-        float v[8];
+    // 32 loads in flight, added in the same order as the plain loop
+    for (; j + 32 <= S.count; j += 32) {
+        float v[32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = p[(j + i) * jstride];
+        for (int i = 0; i < 32; ++i) v[i] = p[(j + i) * S.jstride];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc += v[i];
+        for (int i = 0; i < 32; ++i) acc += v[i];
     }
-    for (; j < count; ++j) acc += p[j * jstride];
-    out[k * out_stride] = acc;
+    for (; j < S.count; ++j) acc += p[j * S.jstride];
+    S.out[k * S.out_stride] = acc;
+}
+
+// Both second passes of the backward in one launch: blocks [0, A.blocks)
+// sum A, the rest sum B (B.blocks may be 0).
+__global__ __launch_bounds__(kBlock) void swiglu_sum_partials_kernel(PartialSum A, PartialSum B) {
+    const int64_t bx = blockIdx.x;
+    if (bx < A.blocks) sum_one(A, bx * kBlock + threadIdx.x);
+    else sum_one(B, (bx - A.blocks) * kBlock + threadIdx.x);
 }
 
 __global__ __launch_bounds__(kBlock) void swiglu_zero_kernel(float* p, int64_t count,
@@ -557,13 +695,15 @@ swiglu_status fwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
 // [part_ds: tiles x waves x rows fp32],
 // each part starting on a 256-byte boundary. tiles is bounded by the
 // single-element access width, so the size does not depend on alignment.
-int64_t bs_groups(int64_t rows) { return (rows + kBsRows - 1) / kBsRows; }
+int64_t bs_groups(int64_t rows, int64_t rows_per_group = kBsRows) {
+    return (rows + rows_per_group - 1) / rows_per_group;
+}
 int64_t bs_max_tiles(int64_t n) { return (n + kBlock - 1) / kBlock; }
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 size_t bs_workspace_bytes(int64_t rows, int64_t n, bool want_db, bool want_ds) {
     int64_t b = 0;
-    if (want_db) b += round256(bs_groups(rows) * 2 * n * 4);
+    if (want_db) b += round256(bs_groups(rows, kMinGroupRows) * 2 * n * 4);
     if (want_ds) b += round256(rows * bs_max_tiles(n) * kWaves * 4);
     return (size_t)b;
 }
@@ -578,12 +718,19 @@ swiglu_status zero_fill(float* p, int64_t count, int64_t stride, hipStream_t str
                : SWIGLU_ERR_HIP;
 }
 
-swiglu_status sum_partials(const float* part, int64_t count, int64_t jstride, int64_t kstride,
-                           int64_t width, float* out, int64_t out_stride, hipStream_t stream) {
-    void* args[] = {&part, &count, &jstride, &kstride, &width, &out, &out_stride};
-    const uint32_t blocks = (uint32_t)((width + kBlock - 1) / kBlock);
+PartialSum partial_sum(const float* part, int64_t count, int64_t jstride, int64_t kstride,
+                       int64_t width, float* out, int64_t out_stride) {
+    return PartialSum{part, count, jstride, kstride, width, out, out_stride,
+                      (width + kBlock - 1) / kBlock};
+}
+
+// The second passes (either may be absent: blocks 0), in one launch.
+swiglu_status sum_partials(PartialSum A, PartialSum B, hipStream_t stream) {
+    const int64_t blocks = A.blocks + B.blocks;
+    if (blocks == 0) return SWIGLU_OK;
+    void* args[] = {&A, &B};
     return hipLaunchKernel(reinterpret_cast<const void*>(&swiglu_sum_partials_kernel),
-                           dim3(blocks), dim3(kBlock), args, 0, stream) == hipSuccess
+                           dim3((uint32_t)blocks), dim3(kBlock), args, 0, stream) == hipSuccess
                ? SWIGLU_OK
                : SWIGLU_ERR_HIP;
 }
@@ -605,6 +752,22 @@ const void* bwd_bs1_kernel_for(bool in_place, bool has_bias, bool has_scale, boo
     }
 }
 
+// The tile backward (dbias wanted, so there is a bias; 16-byte vectors only).
+template <typename T, int VEC>
+const void* bwd_tile_kernel_for(bool in_place, bool has_scale, bool want_ds) {
+    if constexpr (VEC * sizeof(T) != 16) {
+        return nullptr;
+    } else {
+#define SWIGLU_BST(IP, S, D) reinterpret_cast<const void*>(&swiglu_bwd_bs_tile_kernel<T, VEC, IP, true, S, D>)
+#define SWIGLU_BST_S(IP) \
+    (!has_scale ? SWIGLU_BST(IP, false, false) \
+                : want_ds ? SWIGLU_BST(IP, true, true) : SWIGLU_BST(IP, true, false))
+        return in_place ? SWIGLU_BST_S(true) : SWIGLU_BST_S(false);
+#undef SWIGLU_BST_S
+#undef SWIGLU_BST
+    }
+}
+
 // ops: dy, gate, up, dgate, dup.
 template <typename T, int VEC>
 swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, int64_t n,
@@ -612,7 +775,11 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
                             void* workspace, hipStream_t stream) {
     const uint32_t nv = (uint32_t)(n / VEC);
     const uint32_t tiles = (nv + kBlock - 1) / kBlock;
-    const int64_t groups = bs_groups(rows);
+    // With dbias, wide rows of 16-byte vectors take the one-shot tile kernel
+    // (kTileRows rows per partial); the row loop takes the rest.
+    const bool tile = SWIGLU_BS_TILE && dbias != nullptr && nv >= 64u && VEC * sizeof(T) == 16;
+    const int64_t group_rows = tile ? (int64_t)kTileRows : (int64_t)kBsRows;
+    const int64_t groups = bs_groups(rows, group_rows);
     float* part_db = nullptr;
     float* part_ds = nullptr;
     char* ws = static_cast<char*>(workspace);
@@ -636,7 +803,7 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
     G.tiles = tiles;
     G.total_rows = rows;
     // Without dbias, wide rows of 16-byte vectors take the one-shot kernel
-    // (the row loop exists for the dbias column sums).
+    // (the row loop and the tile kernel exist for the dbias column sums).
     const bool one_shot = SWIGLU_BS_ONE_SHOT && dbias == nullptr && nv >= (uint32_t)kBlock &&
                           VEC * sizeof(T) == 16;
     void* args[] = {&dyp, &dys, &gp, &gs, &upp, &us, &dgp, &dgs, &dup, &dus,
@@ -646,7 +813,10 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
     const void* k1 = one_shot ? bwd_bs1_kernel_for<T, VEC>(in_place, bg != nullptr,
                                                            A.scale != nullptr, dscale != nullptr)
                               : nullptr;
-    const int64_t rows_per_launch = one_shot ? (int64_t)kMaxGridY : (int64_t)kMaxGridY * kBsRows;
+    const void* kt = tile ? bwd_tile_kernel_for<T, VEC>(in_place, A.scale != nullptr,
+                                                        dscale != nullptr)
+                          : nullptr;
+    const int64_t rows_per_launch = one_shot ? (int64_t)kMaxGridY : (int64_t)kMaxGridY * group_rows;
     for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
         const int64_t rc = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
         dyp = static_cast<const T*>(ops[0].p) + r0 * dys;
@@ -657,7 +827,7 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
         sc = A.scale != nullptr ? A.scale + r0 * scs : nullptr;
         G.rows = rc;
         G.row0 = r0;
-        G.group0 = r0 / kBsRows;
+        G.group0 = r0 / group_rows;
         if (one_shot) {
             // with a bias, a block takes two rows (see the kernel)
             const uint32_t gy =
@@ -667,17 +837,23 @@ swiglu_status bwd_bs_launch(const Operand* ops, const BsArgs& A, int64_t rows, i
                 return SWIGLU_ERR_HIP;
             continue;
         }
-        const uint32_t gy = (uint32_t)bs_groups(rc);
+        const uint32_t gy = (uint32_t)bs_groups(rc, group_rows);
+        if (tile) {
+            // one block per 64-vector chunk: tiles * kWaves chunks, so that
+            // every dscale partial the second pass reads is written
+            if (hipLaunchKernel(kt, dim3(tiles * kWaves, gy), dim3(kTileThreads), args, 0,
+                                stream) != hipSuccess)
+                return SWIGLU_ERR_HIP;
+            continue;
+        }
         if (hipLaunchKernel(k, dim3(tiles, gy), dim3(kBlock), args, 0, stream) != hipSuccess)
             return SWIGLU_ERR_HIP;
     }
-    swiglu_status st = SWIGLU_OK;
-    if (dbias != nullptr)
-        st = sum_partials(part_db, groups, 2 * n, 1, 2 * n, dbias, 1, stream);
-    if (st == SWIGLU_OK && dscale != nullptr)
-        st = sum_partials(part_ds, (int64_t)tiles * kWaves, rows, 1, rows, dscale, dscale_stride,
-                          stream);
-    return st;
+    PartialSum sdb{}, sds{};
+    if (dbias != nullptr) sdb = partial_sum(part_db, groups, 2 * n, 1, 2 * n, dbias, 1);
+    if (dscale != nullptr)
+        sds = partial_sum(part_ds, (int64_t)tiles * kWaves, rows, 1, rows, dscale, dscale_stride);
+    return sum_partials(sdb, sds, stream);
 }
 
 }  // namespace

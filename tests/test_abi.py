@@ -198,11 +198,15 @@ def test_bias_scale_workspace_size(lib):
     r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
     assert ws(8192, 32768, 0, 0) == 0
     assert ws(0, 32768, 1, 1) == 0 and ws(8, 0, 1, 1) == 0 and ws(-1, 8, 1, 1) == 0
-    groups = (8192 + 127) // 128
+    # dbias: one fp32 partial row of 2n per group of 64 rows (the smaller of
+    # the tile kernel's 64-row and the row loop's 128-row groups); dscale: one
+    # fp32 partial per row and 64-element chunk of the widest plan (1-element
+    # accesses: ceil(n / 256) tiles of 4 chunks)
+    groups = (8192 + 63) // 64
     assert ws(8192, 32768, 1, 0) == r256(groups * 2 * 32768 * 4)
     assert ws(8192, 32768, 0, 1) == r256(8192 * 128 * 4 * 4)
     assert ws(8192, 32768, 1, 1) == r256(groups * 2 * 32768 * 4) + r256(8192 * 128 * 4 * 4)
-    assert ws(300, 1001, 1, 1) == r256(3 * 2002 * 4) + r256(300 * 4 * 4 * 4)
+    assert ws(300, 1001, 1, 1) == r256(5 * 2002 * 4) + r256(300 * 4 * 4 * 4)
 
 
 @no_gpu_only

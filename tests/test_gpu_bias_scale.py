@@ -207,7 +207,8 @@ def test_full_size_workloads_with_bias_and_scale(name):
 @pytest.mark.parametrize("in_place", [False, True])
 def test_one_shot_backward_matches_row_loop(dtype, n, bias, in_place):
     """Without dbias, wide rows of 16-byte vectors take a one-shot kernel;
-    with dbias, the row-loop kernel. dx and dscale must be the same bits."""
+    with dbias, the tile kernel (one-shot too, with the column sums added
+    across waves in LDS). dx and dscale must be the same bits."""
     print(f"[bias/scale one-shot] {dtype} n={n} bias={bias} in_place={in_place}", flush=True)
     x_h, dy_h, b_h, s_h = _make(515, n, dtype, seed=47, bias=bias, scale=True)
     x, dy = gu.to_dev(x_h, dtype), gu.to_dev(dy_h, dtype)
@@ -234,3 +235,46 @@ def test_scale_only_wide_rows_parity(dtype):
     x_h, dy_h, b_h, s_h = _make(300, 4096, dtype, seed=48, bias=False, scale=True)
     _run_and_check(x_h, dy_h, b_h, s_h, dtype)
     _run_and_check(x_h, dy_h, b_h, s_h, dtype, in_place=True)
+
+
+@pytest.mark.parametrize("dtype,rows,n", [("bf16", 777, 1096), ("fp32", 777, 260),
+                                          ("bf16", 64, 512), ("fp32", 129, 4100)])
+@pytest.mark.parametrize("scale", [False, True])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_tile_backward_ragged(dtype, rows, n, scale, in_place):
+    """The dbias backward on 16-byte rows (tile kernel: 64-vector chunks of
+    64-row groups) with a partial last chunk (nv = 137, 65, 1025) and a
+    partial last row group, against the oracle; one exact chunk and group
+    (bf16 64 x 512)."""
+    print(f"[bias/scale tile] {dtype} rows={rows} n={n} scale={scale} in_place={in_place}",
+          flush=True)
+    x_h, dy_h, b_h, s_h = _make(rows, n, dtype, seed=49, bias=True, scale=scale)
+    _run_and_check(x_h, dy_h, b_h, s_h, dtype, in_place=in_place)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tile_and_row_loop_give_the_same_dx(dtype):
+    """The same problem through the tile kernel (16-byte aligned rows) and
+    through the row-loop kernel (the rows moved by one element, so only
+    narrower accesses fit): dx is computed per element by the same function,
+    so it is the same bits; dbias and dscale are summed in other orders and
+    each meets the oracle's bar."""
+    rows, n = 300, 2048
+    x_h, dy_h, b_h, s_h = _make(rows, n, dtype, seed=50)
+    y_ref, dx_ref, db_ref, ds_ref, db_abs, ds_abs = _refs(x_h, dy_h, b_h, s_h, dtype)
+    x, dy = gu.to_dev(x_h, dtype), gu.to_dev(dy_h, dtype)
+    b, s = gu.to_dev(b_h, dtype), torch.from_numpy(s_h).cuda()
+    # misaligned copies: one element into a wider buffer, row stride 2n + 1
+    xm_buf = torch.empty(rows, 2 * n + 1, dtype=x.dtype, device="cuda")
+    xm = xm_buf[:, 1:]
+    xm.copy_(x)
+    dxm_buf = torch.empty(rows, 2 * n + 1, dtype=x.dtype, device="cuda")
+    dxm = dxm_buf[:, 1:]
+    dx_t, db_t, ds_t = sw.swiglu_gateup_bias_scale_bwd(dy, x, b, s)
+    dx_l, db_l, ds_l = sw.swiglu_gateup_bias_scale_bwd(dy, xm, b, s, dx=dxm)
+    torch.cuda.synchronize()
+    assert gu.bits_equal(dx_t, dx_l.contiguous())
+    _check_elem(dx_t, dx_ref, dtype, "dx (tile)")
+    for db, ds, what in ((db_t, ds_t, "tile"), (db_l, ds_l, "row loop")):
+        _check_sum(db, db_ref, db_abs, f"dbias ({what})")
+        _check_sum(ds, ds_ref, ds_abs, f"dscale ({what})")

@@ -84,7 +84,7 @@ def _same(a, b, what):
 
 
 # (rows, n, dtype, want dbias, want dscale, in place): the first call is the
-# 8192 x 32768 bf16 shape with both sums (32 MiB of partials), the next ones
+# 8192 x 32768 bf16 shape with both sums (48 MiB of partials), the next ones
 # are smaller and leave the earlier partials in the scratch.
 CALLS = [
     (8192, 32768, "bf16", True, True, False),
@@ -128,7 +128,7 @@ def test_noalloc_repeated_call_same_bits():
 
 
 def test_noalloc_refuses_problems_past_the_limit():
-    """16384 rows of n = 65536 with both sums need 128 MiB of partials: the
+    """16384 rows of n = 65536 with both sums need 192 MiB of partials: the
     call is refused before any launch (the buffers are real and large enough
     all the same), and the outputs keep their canaries."""
     lib = sw.load_library()
