@@ -21,12 +21,18 @@ Behaviour follows the Liger-Kernel Megatron SwiGLU page:
 * §Background: the two-tensor op for models whose gate and up projections
   are separate tensors.
 
-The fc1 projection with the SwiGLU epilogue (Liger-Kernel test/cute page,
+The fc1 projection followed by the SwiGLU (Liger-Kernel test/cute page,
 §MLP1 numerical reference: fused MLP1-with-activation variants) is wired in
-as Fc1SwiGLU: the forward is the fused kernel, which also writes the
-[tokens, 2n] product for the backward; the backward is the SwiGLU backward
-kernel followed by the two weight and input GEMMs of the projection (plain
-library GEMMs through torch.matmul).
+as Fc1SwiGLU. Its forward either runs the projection as a library GEMM
+(torch.matmul) and then the fused gate-up SwiGLU kernel on the [tokens, 2n]
+product (the default), or, with fused_epilogue=True, the one kernel that
+computes the projection with the SwiGLU as its epilogue and also writes the
+product. The default is the faster of the two on MI355X: with the product
+written (as the backward needs it), the GEMM then the SwiGLU took 5.8 ms
+against 6.4-6.5 ms for the fused kernel at 8192 tokens, hidden 8192 and
+n = 32768, and the two were level at hidden 4096, n = 4096. The backward is
+the SwiGLU backward kernel followed by the two weight and input GEMMs of
+the projection (plain library GEMMs through torch.matmul).
 
 Every SwiGLU computation runs in libswiglu_gateup.so; this module only wires
 it into autograd.
@@ -198,13 +204,20 @@ class MegatronSwiGLU(torch.nn.Module):
 
 class Fc1SwiGLU(torch.autograd.Function):
     """y = silu(a W_g^T) * (a W_u^T) for bf16 a [..., k] and W = [W_g; W_u]
-    [2n, k]. Saves a, W and the product a W^T (written by the fused kernel)."""
+    [2n, k]. Saves a, W and the product a W^T. fused_epilogue: compute it
+    with the fc1 kernel that has the SwiGLU as its epilogue (one launch) rather
+    than a library GEMM followed by the SwiGLU kernel (the default, faster on
+    MI355X at the shapes measured)."""
 
     @staticmethod
-    def forward(ctx, a: torch.Tensor, w: torch.Tensor):
+    def forward(ctx, a: torch.Tensor, w: torch.Tensor, fused_epilogue: bool = False):
         k = w.shape[1]
         a2 = _as_row_view(a.reshape(-1, k))
-        y, x = swiglu_fc1_fwd(a2, w, x_out=True)
+        if fused_epilogue:
+            y, x = swiglu_fc1_fwd(a2, w, x_out=True)
+        else:
+            x = torch.matmul(a2, w.t())                # [m, 2n] = [gate | up]
+            y = swiglu_gateup_fwd(x)
         ctx.save_for_backward(a2, w, x)
         ctx.a_shape = tuple(a.shape)
         return y.reshape(tuple(a.shape[:-1]) + (w.shape[0] // 2,))
@@ -217,25 +230,30 @@ class Fc1SwiGLU(torch.autograd.Function):
         dx = swiglu_gateup_bwd(dy2, x)                 # [m, 2n] = [dgate | dup]
         da = dx @ w if ctx.needs_input_grad[0] else None
         dw = dx.t() @ a2 if ctx.needs_input_grad[1] else None
-        return (da.reshape(ctx.a_shape) if da is not None else None), dw
+        return (da.reshape(ctx.a_shape) if da is not None else None), dw, None
 
 
-def fc1_swiglu(a: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
-    return Fc1SwiGLU.apply(a, w)
+def fc1_swiglu(a: torch.Tensor, w: torch.Tensor, fused_epilogue: bool = False) -> torch.Tensor:
+    return Fc1SwiGLU.apply(a, w, fused_epilogue)
 
 
 class FusedFc1SwiGLU(torch.nn.Module):
     """The first half of a SwiGLU MLP: a bias-free fc1 projection to [gate | up]
-    (weight [2 * ffn_hidden, hidden], the Linear layout) with the SwiGLU fused
-    into its epilogue. bf16 only."""
+    (weight [2 * ffn_hidden, hidden], the Linear layout) followed by the
+    SwiGLU, with no chunk or copy between them. bf16 only. fused_epilogue
+    selects the single fc1 kernel with the SwiGLU in its epilogue; by default
+    the projection is a library GEMM and the SwiGLU the fused gate-up kernel,
+    which measured faster (see Fc1SwiGLU)."""
 
-    def __init__(self, hidden: int, ffn_hidden: int, device=None, dtype=torch.bfloat16):
+    def __init__(self, hidden: int, ffn_hidden: int, device=None, dtype=torch.bfloat16,
+                 fused_epilogue: bool = False):
         super().__init__()
         if dtype != torch.bfloat16:
             raise ValueError("FusedFc1SwiGLU is bf16 only")
+        self.fused_epilogue = fused_epilogue
         self.weight = torch.nn.Parameter(torch.empty(2 * ffn_hidden, hidden, device=device,
                                                      dtype=dtype))
         torch.nn.init.normal_(self.weight, std=hidden ** -0.5)
 
     def forward(self, a: torch.Tensor) -> torch.Tensor:
-        return Fc1SwiGLU.apply(a, self.weight)
+        return Fc1SwiGLU.apply(a, self.weight, self.fused_epilogue)

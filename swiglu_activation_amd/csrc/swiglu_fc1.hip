@@ -17,16 +17,17 @@
 //    4 x 2 for the up projection (256 fp32 accumulators per lane, in the
 //    accumulation registers). Per 16-wide k step a wave reads 8 fragments
 //    from LDS for 16 MFMAs: 1/64 byte of LDS traffic per flop.
-//  * k is walked in tiles of TILE_K (64) through a ring of STAGES (2) LDS
-//    stages, each 256 token rows + 256 weight rows of TILE_K bf16. Global
-//    memory is copied straight into LDS (global_load_lds_dwordx4: no
-//    registers, no LDS write instructions); the copies of the next
-//    STAGES - 1 tiles are in flight while one tile feeds the MFMAs. Each
-//    stage is its own LDS array and the loop is unrolled over the ring, so
-//    the compiler can tell the stage being read from the ones being filled
-//    and waits only where the data is needed. (64-wide tiles in 2 stages
-//    measured faster than 32-wide tiles in 3 to 5: each copy instruction
-//    then reads whole 128-byte lines.)
+//  * k is walked in tiles of 64 through two rings of LDS stages: the token
+//    rows (256 x 64 bf16, 32 KiB) in A_STAGES (2) stages and the weight rows
+//    (256 x 64 bf16) in W_STAGES (3) stages, 160 KiB in all. Global memory
+//    is copied straight into LDS (global_load_lds_dwordx4: no registers, no
+//    LDS write instructions). A tile's token copies are issued right after
+//    the barrier that frees their stage, one tile ahead; its weight copies
+//    (the operand that misses L2 more often: each weight tile is shared by
+//    fewer of the workgroups an L2 serves) W_STAGES - 1 tiles ahead, issued
+//    after the token copies so that a wait for the tokens never waits for
+//    them. Each stage is its own LDS array and the loop is unrolled over
+//    lcm(A_STAGES, W_STAGES) tiles, so every stage is named statically.
 //  * A copy instruction writes 1 KiB of LDS in lane order (rows of
 //    2 TILE_K bytes), so the layout is chosen through the global addresses:
 //    the 16-byte chunks of a row are permuted by an XOR with bits of the
@@ -34,9 +35,11 @@
 //  * The next k step's fragments are read while the current step's MFMAs
 //    run; one barrier per tile hands a filled stage to the readers and an
 //    emptied one to the copies.
-//  * The copies of a tile are spread thinly over two k steps (one every two
-//    MFMAs), not issued in a burst: a burst fills the copy queue, and the
-//    wave, which issues in order, then stalls in front of its next MFMA.
+//  * A tile's copies are spread thinly over one k step each (token copies
+//    over the last step of the tile before, weight copies over the first
+//    step of the tile), not issued in a burst: a burst fills the copy queue,
+//    and the wave, which issues in order, then stalls in front of its next
+//    MFMA.
 //    Each copy is addressed as a wave-uniform base in scalar registers plus
 //    a fixed 32-bit lane offset, so no vector instruction sits between two
 //    copies (which limits lda and ldw to 2^28 elements).
@@ -65,9 +68,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_NT_EPI
 #define SWIGLU_FC_NT_EPI 0      // nontemporal hint on the epilogue's stores
 #endif
-#ifndef SWIGLU_FC_COPYMAP
-#define SWIGLU_FC_COPYMAP 0     // 1: each wave copies a contiguous band of rows
-#endif
 #ifndef SWIGLU_FC_CPOL
 #define SWIGLU_FC_CPOL 0        // cache-policy bits of the copies (gfx950: 1 sc0, 2 nt)
 #endif
@@ -77,10 +77,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_SADDR
 #define SWIGLU_FC_SADDR 1       // copies as a wave-uniform base (SGPRs) plus a fixed 32-bit lane offset
 #endif
-#ifndef SWIGLU_FC_SPREAD
-#define SWIGLU_FC_SPREAD 2      // copy issue: 0 packed early in the step after the barrier; N >= 1
-#endif                          // spread evenly over that step and the next N - 1 steps
-
 #ifndef SWIGLU_FC_WAVES
 #define SWIGLU_FC_WAVES 4       // waves per workgroup: 4 (128 x 64 wave tiles) or 8 (64 x 64)
 #endif
@@ -94,38 +90,36 @@ constexpr int kFcMT = kFcWaveT / 32;                 // 32x32 tiles per wave alo
 constexpr int kFcMF = kFcWaveF / 32;                 // ... along features (each: gate + up)
 constexpr int kFcTileT = kFcWaveT * kFcWavesT;       // tokens per workgroup
 constexpr int kFcTileF = kFcWaveF * kFcWavesF;       // features per workgroup
-#ifndef SWIGLU_FC_TILE_K
-#define SWIGLU_FC_TILE_K 64     // k per stage (32 or 64)
+constexpr int kFcTileK = 64;                         // k per stage
+#ifndef SWIGLU_FC_A_STAGES
+#define SWIGLU_FC_A_STAGES 2    // LDS stages of token rows
 #endif
-constexpr int kFcTileK = SWIGLU_FC_TILE_K;           // k per stage
-#ifndef SWIGLU_FC_STAGES
-#define SWIGLU_FC_STAGES 2      // LDS stages in the ring (2 to 5; x k per stage <= 160 KiB)
+#ifndef SWIGLU_FC_W_STAGES
+#define SWIGLU_FC_W_STAGES 3    // LDS stages of weight rows (2 or 3)
 #endif
-constexpr int kFcStages = SWIGLU_FC_STAGES;
+constexpr int kFcAStages = SWIGLU_FC_A_STAGES, kFcWStages = SWIGLU_FC_W_STAGES;
+static_assert(kFcAStages == 2 && (kFcWStages == 2 || kFcWStages == 3), "ring sizes");
+constexpr int kFcPeriod = kFcWStages == 3 ? 6 : 2;    // lcm of the ring sizes
 constexpr int kFcRowsA = kFcTileT;                   // token rows per stage
-constexpr int kFcRows = kFcTileT + 2 * kFcTileF;     // + gate rows + up rows
+constexpr int kFcRowsW = 2 * kFcTileF;               // gate rows + up rows per stage
 constexpr int kFcRowElems = kFcTileK;                // bf16 per LDS row (no padding)
-constexpr int kFcStageElems = kFcRows * kFcRowElems;
+constexpr int kFcAElems = kFcRowsA * kFcRowElems;
+constexpr int kFcWElems = kFcRowsW * kFcRowElems;
 constexpr int kFcChunks = kFcTileK / 8;              // 16-byte chunks per row
 constexpr int kFcCopyRows = 64 / kFcChunks;          // rows per copy instruction (one wave)
-constexpr int kFcCopies = kFcRows / kFcCopyRows / kFcWaves;   // copies per thread per tile
+constexpr int kFcCopiesA = kFcRowsA / kFcCopyRows / kFcWaves;   // token copies per thread per tile
+constexpr int kFcCopiesW = kFcRowsW / kFcCopyRows / kFcWaves;   // weight copies ...
+constexpr int kFcCopies = kFcCopiesA + kFcCopiesW;
 constexpr int kFcMfma = 2 * kFcMF * kFcMT;           // MFMAs per wave per k step
 constexpr int kFcReads = kFcMT + 2 * kFcMF;          // fragment reads per k step
 constexpr int kFcSteps = kFcTileK / 16;              // MFMA k steps per stage
 constexpr int64_t kFcMaxLd = (int64_t)1 << 28;      // largest lda / ldw (elements)
-constexpr int kFcSpread = SWIGLU_FC_SPREAD > 0 ? SWIGLU_FC_SPREAD : 1;   // steps a tile's copies span
-// The rest of a tile's copies go into the next slot's steps before its last
-// one (steps 0 and 1 of four, step 0 of two); with two stages that slot's
-// wait needs them, so at least one step must follow.
-static_assert(kFcSpread <= (kFcSteps == 4 ? 3 : 2) && (kFcStages > 2 || kFcSpread <= kFcSteps - 1),
-              "a tile's copies are all issued before the wait that needs them");
-// First copy issued in step j of the span (j = 0: the step after the barrier).
-constexpr int copy_begin(int j) { return j * kFcCopies / kFcSpread; }
-static_assert(kFcTileK == 32 || kFcTileK == 64, "4 or 8 chunks per row");
-static_assert(kFcSteps % 2 == 0, "fragment sets alternate within a stage");
-static_assert(kFcCopies * kFcWaves * kFcCopyRows == kFcRows, "whole copies per stage");
-static_assert(kFcRowsA % kFcCopyRows == 0 && kFcTileF % kFcCopyRows == 0, "copies do not straddle");
-static_assert(kFcStages * kFcStageElems * 2 <= 160 * 1024, "the ring must fit in LDS");
+static_assert(kFcSteps == 4, "four k steps per tile");
+static_assert(kFcCopiesA * kFcWaves * kFcCopyRows == kFcRowsA &&
+                  kFcCopiesW * kFcWaves * kFcCopyRows == kFcRowsW, "whole copies per stage");
+static_assert(kFcTileF % kFcCopyRows == 0, "copies do not straddle gate and up rows");
+static_assert((kFcAStages * kFcAElems + kFcWStages * kFcWElems) * 2 <= 160 * 1024,
+              "the rings must fit in LDS");
 
 struct Fc1Args {
     const uint16_t* a;   // [m, k] tokens, row stride lda
@@ -136,35 +130,36 @@ struct Fc1Args {
     int64_t m, n, k;
 };
 
-// The LDS ring: one array per stage.
-static_assert(kFcStages >= 2 && kFcStages <= 5, "ring size");
-__shared__ __attribute__((aligned(16))) uint16_t fc_stage0[kFcStageElems];
-__shared__ __attribute__((aligned(16))) uint16_t fc_stage1[kFcStageElems];
-__shared__ __attribute__((aligned(16))) uint16_t fc_stage2[kFcStageElems];
-__shared__ __attribute__((aligned(16))) uint16_t fc_stage3[kFcStageElems];
-#if SWIGLU_FC_STAGES == 5
-__shared__ __attribute__((aligned(16))) uint16_t fc_stage4[kFcStageElems];
-#endif
+// The LDS rings: one array per stage.
+__shared__ __attribute__((aligned(16))) uint16_t fc_a0[kFcAElems];
+__shared__ __attribute__((aligned(16))) uint16_t fc_a1[kFcAElems];
+__shared__ __attribute__((aligned(16))) uint16_t fc_w0[kFcWElems];
+__shared__ __attribute__((aligned(16))) uint16_t fc_w1[kFcWElems];
+__shared__ __attribute__((aligned(16))) uint16_t fc_w2[kFcWElems];
 
 template <int S>
-__device__ __forceinline__ uint16_t* stage() {
-    static_assert(S >= 0 && S < kFcStages, "stage index");
-    if constexpr (S == 0) return fc_stage0;
-    else if constexpr (S == 1) return fc_stage1;
-    else if constexpr (S == 2) return fc_stage2;
-    else if constexpr (S == 3) return fc_stage3;
-#if SWIGLU_FC_STAGES == 5
-    else return fc_stage4;
-#endif
+__device__ __forceinline__ uint16_t* stage_a() {
+    static_assert(S >= 0 && S < kFcAStages, "stage index");
+    if constexpr (S == 0) return fc_a0;
+    else return fc_a1;
 }
 
-// Stage s, chosen at run time (0 <= s < stages).
-__device__ __forceinline__ uint16_t* stage_at(int s) {
-    uint16_t* p = stage<0>();
-    if (s == 1) p = stage<1>();
-    if constexpr (kFcStages > 2) if (s == 2) p = stage<2 % kFcStages>();
-    if constexpr (kFcStages > 3) if (s == 3) p = stage<3 % kFcStages>();
-    if constexpr (kFcStages > 4) if (s == 4) p = stage<4 % kFcStages>();
+template <int S>
+__device__ __forceinline__ uint16_t* stage_w() {
+    static_assert(S >= 0 && S < kFcWStages, "stage index");
+    if constexpr (S == 0) return fc_w0;
+    else if constexpr (S == 1) return fc_w1;
+    else return fc_w2;
+}
+
+// The epilogue's staging area of wave w: one stage array per wave (each
+// holds at least a wave's 128 x 72 staging tile).
+__device__ __forceinline__ uint16_t* epi_region(int w) {
+    uint16_t* p = stage_a<0>();
+    if (w == 1) p = stage_a<1>();
+    if (w == 2) p = stage_w<0>();
+    if (w == 3) p = stage_w<1>();
+    if constexpr (kFcWStages > 2) if (w == 4) p = stage_w<2 % kFcWStages>();
     return p;
 }
 
@@ -176,14 +171,13 @@ __device__ __forceinline__ int chunk_slot(int r, int c) {
     else return c ^ ((r >> 1) & 7);
 }
 
-// The block of kFcCopyRows LDS rows that copy i of a wave fills: the waves
-// interleave block by block (COPYMAP 0) or each takes a contiguous band.
+// The block of kFcCopyRows LDS rows that copy i of a wave fills, in the
+// combined row space (token rows [0, kFcRowsA), then gate and up rows):
+// copies [0, kFcCopiesA) take token rows and the rest weight rows, and the
+// waves interleave block by block.
 __device__ __forceinline__ int copy_block(int i, int wave) {
-#if SWIGLU_FC_COPYMAP
-    return wave * kFcCopies + i;
-#else
-    return i * kFcWaves + wave;
-#endif
+    if (i < kFcCopiesA) return i * kFcWaves + wave;
+    return kFcRowsA / kFcCopyRows + (i - kFcCopiesA) * kFcWaves + wave;
 }
 
 // Source row of each of this thread's copies, at k = 0. Copy i of a wave
@@ -249,32 +243,42 @@ __device__ __forceinline__ void make_sources(const Fc1Args& P, int64_t t0, int64
 #endif
 }
 
-// Starts copies [I0, I1) of k tile t into stage S.
-template <int S, int I0 = 0, int I1 = kFcCopies>
-__device__ __forceinline__ void copy_tile(const Sources& src, int t) {
+// One copy: 16 bytes per lane of tile t, from the lane's source into the
+// 1 KiB block of LDS at dst.
+__device__ __forceinline__ void copy_one(const Sources& src, int i, int t, uint16_t* dst) {
 #if SWIGLU_FC_SADDR
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tb = (int64_t)t * kFcTileK * 2;                  // the tile's byte offset
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        uint16_t* dst = stage<S>() + copy_block(i, wave) * kFcCopyRows * kFcRowElems;
-        // (the offset is made opaque in place, so that the compiler neither
-        // folds base and offset into one loop-invariant vector pointer nor
-        // copies the offset into a scratch register for each copy)
-        asm volatile("" : "+v"(src.off[i]));
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.base[i] + tb + src.off[i]),
-                                         (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
-    }
+    // (the offset is made opaque in place, so that the compiler neither
+    // folds base and offset into one loop-invariant vector pointer nor
+    // copies the offset into a scratch register for each copy)
+    asm volatile("" : "+v"(src.off[i]));
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.base[i] + tb + src.off[i]),
+                                     (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
 #else
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        uint16_t* dst = stage<S>() + copy_block(i, wave) * kFcCopyRows * kFcRowElems;
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const void*>(src.p[i] + (int64_t)t * kFcTileK),
-            (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
-    }
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.p[i] + (int64_t)t * kFcTileK),
+                                     (lds_void*)(dst), 16, 0, SWIGLU_FC_CPOL);
 #endif
+}
+
+// Starts token copies [I0, I1) of k tile t into token stage S.
+template <int S, int I0 = 0, int I1 = kFcCopiesA>
+__device__ __forceinline__ void copy_a(const Sources& src, int t) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+        copy_one(src, i, t, stage_a<S>() + copy_block(i, wave) * kFcCopyRows * kFcRowElems);
+}
+
+// Starts weight copies [I0, I1) (counted among the weight copies) of k tile
+// t into weight stage S.
+template <int S, int I0 = 0, int I1 = kFcCopiesW>
+__device__ __forceinline__ void copy_w(const Sources& src, int t) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = I0; j < I1; ++j) {
+        const int q = copy_block(kFcCopiesA + j, wave) - kFcRowsA / kFcCopyRows;
+        copy_one(src, kFcCopiesA + j, t, stage_w<S>() + q * kFcCopyRows * kFcRowElems);
+    }
 }
 
 // s_waitcnt: at most N copies (vector memory operations) outstanding, and
@@ -326,15 +330,16 @@ struct Frags {
 
 // off: this lane's element offset for the step (its row within a 32-row
 // tile, and the swizzled slot of its chunk).
-template <int S>
+template <int SA, int SW>
 __device__ __forceinline__ void load_frags(int wt, int wf, int off, Frags& F) {
-    const uint16_t* base = stage<S>();
+    const uint16_t* ta = stage_a<SA>();
+    const uint16_t* tw = stage_w<SW>();
 #pragma unroll
-    for (int j = 0; j < kFcMT; ++j) F.a[j] = frag(base + (wt + 32 * j) * kFcRowElems + off);
+    for (int j = 0; j < kFcMT; ++j) F.a[j] = frag(ta + (wt + 32 * j) * kFcRowElems + off);
 #pragma unroll
     for (int i = 0; i < kFcMF; ++i) {
-        F.g[i] = frag(base + (kFcRowsA + wf + 32 * i) * kFcRowElems + off);
-        F.u[i] = frag(base + (kFcRowsA + kFcTileF + wf + 32 * i) * kFcRowElems + off);
+        F.g[i] = frag(tw + (wf + 32 * i) * kFcRowElems + off);
+        F.u[i] = frag(tw + (kFcTileF + wf + 32 * i) * kFcRowElems + off);
     }
 }
 
@@ -359,22 +364,6 @@ __device__ __forceinline__ void sched_reads_among_mfma() {
 #if SWIGLU_FC_SCHED
 #pragma unroll
     for (int q = 0; q < kFcReads; ++q) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, kFcMfma - kFcReads, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#endif
-}
-
-template <int kUnused = 0>
-__device__ __forceinline__ void sched_copies_reads_among_mfma() {
-#if SWIGLU_FC_SCHED
-    constexpr int per = kFcCopies / kFcReads;        // copies per fragment read
-    static_assert(kUnused != 0 || per * kFcReads == kFcCopies, "copies spread evenly over the reads");
-#pragma unroll
-    for (int q = 0; q < kFcReads; ++q) {
-        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, per, 0);
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
@@ -420,15 +409,14 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t f_tiles, uint32_t t
 }
 
 // Epilogue staging: a wave's tile (kFcWaveT tokens x 64 features of one output)
-// in LDS rows of 72 bf16 (144 bytes, 16-byte aligned rows).
+// in LDS rows of 72 bf16 (144 bytes, 16-byte aligned rows), in the stage
+// arrays once the k loop is done: kEpiPer regions per array.
 constexpr int kEpiPitch = kFcWaveF + 8;
 constexpr int kEpiRegion = kFcWaveT * kEpiPitch;
-// Regions per stage (at most half the waves, so that they spread over two
-// or more stages) and the stages they take.
-constexpr int kEpiPerStage = kFcStageElems / kEpiRegion < kFcWaves / 2 ? kFcStageElems / kEpiRegion
-                                                                         : kFcWaves / 2;
+constexpr int kEpiPer = kFcAElems / kEpiRegion;      // (token and weight stages are the same size)
+static_assert(kFcAElems == kFcWElems, "stage arrays of one size");
 static_assert(!SWIGLU_FC_LDS_EPI ||
-                  (kEpiPerStage >= 1 && (kFcWaves + kEpiPerStage - 1) / kEpiPerStage <= kFcStages),
+                  (kEpiPer >= 1 && (kFcWaves + kEpiPer - 1) / kEpiPer <= kFcAStages + kFcWStages),
               "every wave's region fits in the stages");
 
 // Writes the wave's kFcWaveT x 64 tile of one output, value(i, j, e) for
@@ -474,95 +462,97 @@ struct Ctx {
     Sources src;
     int wt, wf;
     int off[kFcSteps];   // this lane's fragment offset in each k step
-    int kt_count;   // k tiles
-    int pad;        // leading padding tiles that round the count up to the ring size
+    int kt_count;        // k tiles
+    int pad;             // slots skipped at the start so that the slot count is a whole
+                         // number of periods: real tile t is slot t + pad
 };
 
-// Source tile of ring slot kt: padding slots and slots past the end are
-// clamped to a real tile (their copies land in stages whose data is never
-// multiplied in).
+// Source tile of slot kt; slots past the end are clamped to the last tile
+// (their copies land in stages that are never multiplied in).
 __device__ __forceinline__ int source_tile(const Ctx& c, int kt) {
     const int t = kt - c.pad;
     return t < 0 ? 0 : t < c.kt_count ? t : c.kt_count - 1;
 }
 
-// The fragments with the token operand zeroed when `live` is false, so a
-// padding tile adds nothing.
-__device__ __forceinline__ Frags masked(const Frags& F, bool live) {
-    Frags r = F;
-#pragma unroll
-    for (int j = 0; j < kFcMT; ++j) r.a[j] = live ? F.a[j] : bf16x8{};
-    return r;
-}
-
-// Ring slot kt (tile kt - pad), held in stage S = kt % stages. Entering: F0
-// holds (or is receiving) the slot's first-step fragments, and the copies of
-// the following slots up to kt + stages - 1 are in flight or done. The first step's MFMAs run
-// while the second step's fragments are read. Then: wait for slot kt + 1,
-// barrier (slot kt + 1 is complete for every wave, and stage S has been read
-// by every wave), start the copies of slot kt + stages into stage S and read slot
-// kt + 1's first-step fragments while the second step's MFMAs run. After the
-// last slot these extra copies and reads are not used.
-// One k step of stage S with fragments C while the next step's are read
-// into N.
-template <int S, int STEP>
-__device__ __forceinline__ void inner_step(const Ctx& c, bool live, Frags& C, Frags& N, Acc& acc) {
-    load_frags<S>(c.wt, c.wf, c.off[STEP + 1], N);
-    mfma_step(masked(C, live), acc);
+// One k step of tile (SA, SW) with fragments C while the next step's are
+// read into N.
+template <int SA, int SW, int STEP>
+__device__ __forceinline__ void inner_step(const Ctx& c, Frags& C, Frags& N, Acc& acc) {
+    load_frags<SA, SW>(c.wt, c.wf, c.off[STEP + 1], N);
+    mfma_step(C, acc);
     sched_reads_among_mfma();
 }
 
-// inner_step that also issues copies [I0, I1) of slot ts into stage SP,
-// spread over the step's MFMAs.
-template <int S, int STEP, int SP, int I0, int I1>
-__device__ __forceinline__ void copy_step(const Ctx& c, bool live, int ts, Frags& C, Frags& N,
-                                          Acc& acc) {
-    copy_tile<SP, I0, I1>(c.src, source_tile(c, ts));
-    load_frags<S>(c.wt, c.wf, c.off[STEP + 1], N);
-    mfma_step(masked(C, live), acc);
-    sched_mix_at<I1 - I0>();
-}
+// Copies that may still be in flight when slot kt + 1 must be complete: the
+// token copies of slot kt + 1 were issued at the end of tile kt - 1, and
+// with three weight stages only the weight copies issued by tile kt itself
+// (of slot kt + 2) come after them.
+constexpr int kWaitSlot = kFcWStages == 3 ? kFcCopiesW : 0;
 
-// MASK: the slot may be a padding slot (only in the first pass over the ring).
-template <int S, bool MASK>
+// Slot kt at position J of the period: token stage J % A_STAGES, weight
+// stage J % W_STAGES. Entering: F0 holds (or is receiving) the tile's first
+// step's fragments; the token copies of slots up to kt + 1 and the weight
+// copies of slots up to kt + W_STAGES - 2 are issued. Step 0 issues the
+// weight copies of slot kt - 1 + W_STAGES into the weight stage that tile
+// kt - 1 freed; steps 1 and 2 only compute; then wait for slot kt + 1 and
+// barrier (every wave has read this tile's stages into registers), and step
+// 3 issues the token copies of slot kt + A_STAGES into this tile's token
+// stage while slot kt + 1's first fragments are read.
+template <int J>
 __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
-    constexpr int SN = (S + 1) % kFcStages;
-    const bool live = !MASK || kt >= c.pad;
-    // Steps 0 .. spread - 2 also issue the rest of the previous slot's
-    // copies, into the stage that slot freed (there is none before slot 0).
-    constexpr bool kTail = !(MASK && S == 0);
-    constexpr int SP = (S + kFcStages - 1) % kFcStages;
-    if constexpr (kTail && kFcSpread >= 2)
-        copy_step<S, 0, SP, copy_begin(1), copy_begin(2)>(c, live, kt - 1 + kFcStages, F0, F1, acc);
-    else
-        inner_step<S, 0>(c, live, F0, F1, acc);
-    if constexpr (kFcSteps == 4) {
-        if constexpr (kTail && kFcSpread >= 3)
-            copy_step<S, 1, SP, copy_begin(2), copy_begin(3)>(c, live, kt - 1 + kFcStages, F1, F0, acc);
-        else
-            inner_step<S, 1>(c, live, F1, F0, acc);
-        inner_step<S, 2>(c, live, F0, F1, acc);
-    }
-    wait_copies_and_lds<(kFcStages - 2) * kFcCopies>();  // slots kt + 2 .. may be pending
+    constexpr int SA = J % kFcAStages, SW = J % kFcWStages;
+    constexpr int SWP = (J + kFcPeriod - 1) % kFcWStages;     // tile kt - 1's weight stage
+    constexpr int SAN = (J + 1) % kFcAStages, SWN = (J + 1) % kFcWStages;
+    copy_w<SWP>(c.src, source_tile(c, kt - 1 + kFcWStages));
+    load_frags<SA, SW>(c.wt, c.wf, c.off[1], F1);
+    mfma_step(F0, acc);
+    sched_mix_at<kFcCopiesW>();
+    inner_step<SA, SW, 1>(c, F1, F0, acc);
+    inner_step<SA, SW, 2>(c, F0, F1, acc);
+    wait_copies_and_lds<kWaitSlot>();
     ring_barrier();
-    copy_tile<S, 0, copy_begin(1)>(c.src, source_tile(c, kt + kFcStages));
-    load_frags<SN>(c.wt, c.wf, c.off[0], F0);
-    mfma_step(masked(F1, live), acc);
-#if SWIGLU_FC_SPREAD == 0
-    sched_copies_reads_among_mfma();
-#else
-    sched_mix_at<copy_begin(1)>();
-#endif
+    copy_a<SA>(c.src, source_tile(c, kt + kFcAStages));
+    load_frags<SAN, SWN>(c.wt, c.wf, c.off[0], F0);
+    mfma_step(F1, acc);
+    sched_mix_at<kFcCopiesA>();
 }
 
-// Slots kt .. kt + stages - 1: one pass over the ring.
-template <bool MASK>
-__device__ __forceinline__ void ring_pass(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
-    k_tile<0, MASK>(c, kt, F0, F1, acc);
-    k_tile<1, MASK>(c, kt + 1, F0, F1, acc);
-    if constexpr (kFcStages > 2) k_tile<2 % kFcStages, MASK>(c, kt + 2, F0, F1, acc);
-    if constexpr (kFcStages > 3) k_tile<3 % kFcStages, MASK>(c, kt + 3, F0, F1, acc);
-    if constexpr (kFcStages > 4) k_tile<4 % kFcStages, MASK>(c, kt + 4, F0, F1, acc);
+// A whole period of slots from kt (a multiple of the period).
+__device__ __forceinline__ void full_pass(const Ctx& c, int kt, Frags& F0, Frags& F1, Acc& acc) {
+    k_tile<0>(c, kt, F0, F1, acc);
+    k_tile<1 % kFcPeriod>(c, kt + 1, F0, F1, acc);
+    if constexpr (kFcPeriod > 2) {
+        k_tile<2 % kFcPeriod>(c, kt + 2, F0, F1, acc);
+        k_tile<3 % kFcPeriod>(c, kt + 3, F0, F1, acc);
+        k_tile<4 % kFcPeriod>(c, kt + 4, F0, F1, acc);
+        k_tile<5 % kFcPeriod>(c, kt + 5, F0, F1, acc);
+    }
+}
+
+// The first period: slots pad .. period - 1 (the same branch in every wave).
+__device__ __forceinline__ void first_pass(const Ctx& c, Frags& F0, Frags& F1, Acc& acc) {
+    if (c.pad <= 0) k_tile<0>(c, 0, F0, F1, acc);
+    if (c.pad <= 1) k_tile<1 % kFcPeriod>(c, 1, F0, F1, acc);
+    if constexpr (kFcPeriod > 2) {
+        if (c.pad <= 2) k_tile<2 % kFcPeriod>(c, 2, F0, F1, acc);
+        if (c.pad <= 3) k_tile<3 % kFcPeriod>(c, 3, F0, F1, acc);
+        if (c.pad <= 4) k_tile<4 % kFcPeriod>(c, 4, F0, F1, acc);
+        if (c.pad <= 5) k_tile<5 % kFcPeriod>(c, 5, F0, F1, acc);
+    }
+}
+
+// Fill for a first slot P: token copies of slots P and P + 1, weight copies
+// of slots P .. P + W_STAGES - 2 (slot P + W_STAGES - 1's are issued by tile
+// P itself); wait for slot P, barrier, and read its first fragments.
+template <int P>
+__device__ __forceinline__ void prologue(const Ctx& c, Frags& F0) {
+    copy_a<P % kFcAStages>(c.src, source_tile(c, P));
+    copy_w<P % kFcWStages>(c.src, source_tile(c, P));
+    copy_a<(P + 1) % kFcAStages>(c.src, source_tile(c, P + 1));
+    if constexpr (kFcWStages == 3) copy_w<(P + 1) % kFcWStages>(c.src, source_tile(c, P + 1));
+    wait_copies_and_lds<kFcCopiesA + (kFcWStages == 3 ? kFcCopiesW : 0)>();
+    ring_barrier();
+    load_frags<P % kFcAStages, P % kFcWStages>(c.wt, c.wf, c.off[0], F0);
 }
 
 __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint32_t f_tiles,
@@ -587,7 +577,7 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     c.wf = (wave % kFcWavesF) * kFcWaveF;            // wave's feature offset
     c.wt = (wave / kFcWavesF) * kFcWaveT;            // wave's token offset
     c.kt_count = (int)(P.k / kFcTileK);
-    const int slots = (c.kt_count + kFcStages - 1) / kFcStages * kFcStages;
+    const int slots = (c.kt_count + kFcPeriod - 1) / kFcPeriod * kFcPeriod;
     c.pad = slots - c.kt_count;
     {
         // A fragment lane reads row lane % 32 of a 32-row tile and chunk
@@ -598,21 +588,17 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
             c.off[st] = frow * kFcRowElems + chunk_slot(frow, 2 * st + lane / 32) * 8;
     }
 
-    // Fill the ring and wait for slot 0.
-    copy_tile<0>(c.src, source_tile(c, 0));
-    copy_tile<1>(c.src, source_tile(c, 1));
-    if constexpr (kFcStages > 2) copy_tile<2 % kFcStages>(c.src, source_tile(c, 2));
-    if constexpr (kFcStages > 3) copy_tile<3 % kFcStages>(c.src, source_tile(c, 3));
-    if constexpr (kFcStages > 4) copy_tile<4 % kFcStages>(c.src, source_tile(c, 4));
-    wait_copies_and_lds<(kFcStages - 1) * kFcCopies>();
-    ring_barrier();
     Frags F0, F1;
-    load_frags<0>(c.wt, c.wf, c.off[0], F0);
-
-    // unrolled over the ring so that every stage is named statically
-    // the padding slots all fall in the first pass, the only one that masks
-    ring_pass<true>(c, 0, F0, F1, acc);
-    for (int kt = kFcStages; kt < slots; kt += kFcStages) ring_pass<false>(c, kt, F0, F1, acc);
+    switch (c.pad) {
+        case 0: prologue<0>(c, F0); break;
+        case 1: prologue<1 % kFcPeriod>(c, F0); break;
+        case 2: prologue<2 % kFcPeriod>(c, F0); break;
+        case 3: prologue<3 % kFcPeriod>(c, F0); break;
+        case 4: prologue<4 % kFcPeriod>(c, F0); break;
+        default: prologue<5 % kFcPeriod>(c, F0); break;
+    }
+    first_pass(c, F0, F1, acc);
+    for (int kt = kFcPeriod; kt < slots; kt += kFcPeriod) full_pass(c, kt, F0, F1, acc);
     // No copy may still be writing LDS when the workgroup ends.
     wait_copies_and_lds<0>();
 
@@ -621,7 +607,7 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     // output into a private LDS region in registers' order, then reads it
     // back by rows, so each store instruction writes 8 rows of 128 bytes.
     ring_barrier();                                   // every wave is done with the stages
-    uint16_t* region = stage_at(wave / kEpiPerStage) + (wave % kEpiPerStage) * kEpiRegion;
+    uint16_t* region = epi_region(wave / kEpiPer) + (wave % kEpiPer) * kEpiRegion;
     const int64_t tw = t0 + c.wt, fw = f0 + c.wf;     // the wave's first token and feature
     epi_out(region, tw, fw, P.m, P.n, P.y, P.ldy, [&](int i, int j, int e) {
         const float g = acc.g[i][j][e];

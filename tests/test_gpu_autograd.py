@@ -172,12 +172,14 @@ def test_two_tensor_autograd_and_errors():
         sw.swiglu_silu_mul_bwd(dy, gate.detach(), up.detach(), dgate=dy)   # dgate overlaps dy
 
 
-def test_fc1_swiglu_autograd_matches_float64_reference():
-    """Fc1SwiGLU (fused fc1 + SwiGLU forward, SwiGLU backward kernel and two
-    GEMMs in the backward) against float64 CPU autograd of the same bf16
-    inputs. The GPU chain rounds three times to bf16 on the way (the product,
-    [dgate | dup], and the GEMM outputs), each 2^-9 relative; the bar is 1e-2
-    of the reference's norm, per output."""
+@pytest.mark.parametrize("fused_epilogue", [False, True])
+def test_fc1_swiglu_autograd_matches_float64_reference(fused_epilogue):
+    """Fc1SwiGLU (forward: a library GEMM then the SwiGLU kernel, or the fc1
+    kernel with the SwiGLU epilogue; backward: the SwiGLU backward kernel and
+    two GEMMs) against float64 CPU autograd of the same bf16 inputs. The GPU
+    chain rounds three times to bf16 on the way (the product, [dgate | dup],
+    and the GEMM outputs), each 2^-9 relative; the bar is 1e-2 of the
+    reference's norm, per output."""
     from swiglu_activation_amd.autograd import FusedFc1SwiGLU, fc1_swiglu
     rng = np.random.default_rng(70)
     T, h, f = 2 * 96, 256, 192
@@ -191,7 +193,7 @@ def test_fc1_swiglu_autograd_matches_float64_reference():
     (y64 * torch.from_numpy(oracle.widen(g_h, "bf16"))).sum().backward()
     a = gu.to_dev(a_h, "bf16").reshape(2, 96, h).requires_grad_(True)
     w = gu.to_dev(w_h, "bf16").requires_grad_(True)
-    y = fc1_swiglu(a, w)
+    y = fc1_swiglu(a, w, fused_epilogue=fused_epilogue)
     assert y.shape == (2, 96, f)
     y.backward(gu.to_dev(g_h, "bf16").reshape(2, 96, f))
     torch.cuda.synchronize()
@@ -200,7 +202,7 @@ def test_fc1_swiglu_autograd_matches_float64_reference():
         err = (got.double().cpu() - ref).norm() / ref.norm()
         print(f"    {what}: normwise relative error {err.item():.3g}", flush=True)
         assert err < 1e-2, (what, err.item())
-    m = FusedFc1SwiGLU(h, f, device="cuda")
+    m = FusedFc1SwiGLU(h, f, device="cuda", fused_epilogue=fused_epilogue)
     out = m(a.detach())
     out.float().sum().backward()
     torch.cuda.synchronize()
