@@ -130,9 +130,9 @@ __global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
             for (int i = 0; i < VEC; ++i) {
                 g[i] += b[i];
                 u[i] += d[i];
-                float sig, osig;
-                sigmoid_pair<T, false>(g[i], sig, osig);
-                out[i] = HAS_SCALE ? ((g[i] * sig) * u[i]) * s : (g[i] * sig) * u[i];
+                float sig, osig, scl;
+                sigmoid_pair<T, false>(g[i], sig, osig, scl);
+                out[i] = HAS_SCALE ? ((g[i] * sig) * (u[i] * s)) * scl : ((g[i] * sig) * u[i]) * scl;
             }
             Vec<T, VEC>::store(dst, out);
         };
@@ -170,9 +170,9 @@ __global__ __launch_bounds__(kBlock) void swiglu_fwd_bs_kernel(
     }
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-        float sig, osig;
-        sigmoid_pair<T, false>(g[i], sig, osig);
-        out[i] = HAS_SCALE ? ((g[i] * sig) * u[i]) * s : (g[i] * sig) * u[i];
+        float sig, osig, scl;
+        sigmoid_pair<T, false>(g[i], sig, osig, scl);
+        out[i] = HAS_SCALE ? ((g[i] * sig) * (u[i] * s)) * scl : ((g[i] * sig) * u[i]) * scl;
     }
     Vec<T, VEC>::store(y + row * ys + c, out);
 }
@@ -223,14 +223,14 @@ __device__ __forceinline__ void bwd_bs_elem(float g, float u, float d, float bg,
     float zg, zlo;
     two_sum(g, bg, zg, zlo);
     const float zu = u + bu;
-    float sig, osig;
-    sigmoid_pair<T, true>(zg, sig, osig);
+    float sig, osig, scl;
+    sigmoid_pair<T, true>(zg, sig, osig, scl);
     const float h = h_factor_lo<T>(zg, zlo, osig);
-    const float silu = zg * sig;
+    const float silu = zg * sig;                    // times 1/scl, as sig
     const float ds_ = d * s;
-    du = ds_ * silu;
-    dg = ((ds_ * zu) * sig) * h;
-    p = __builtin_fmaf(d * silu, zu, p);
+    du = (ds_ * silu) * scl;
+    dg = ((ds_ * zu) * (sig * h)) * scl;           // sigma h = silu'(z) first: |.| <= 1.1
+    p = __builtin_fmaf((d * silu) * scl, zu, p);
 }
 
 template <typename T, int VEC, bool IN_PLACE>

@@ -145,30 +145,37 @@ __device__ __forceinline__ void sigmoid_fast(float g, float& sig, float& osig) {
 // 2^{-a log2 e}: the product is split so the exponent keeps ~48 bits, the
 // hardware 2^x does the rest, and the tail of the exponent is applied as a
 // first-order correction. The hardware 2^x does not return subnormal
-// results, so arguments below -126 are lifted by 64 and scaled back by an
-// exact multiply, which rounds correctly into the subnormal range.
-__device__ __forceinline__ float exp_neg(float a) {
+// results, so for arguments below -126 the exponent is lifted by 64 (exact)
+// and the result is returned as e^{-a} 2^64 with `tiny` set: the caller
+// scales it back by an exact multiply wherever that rounds best.
+__device__ __forceinline__ float exp_neg_scaled(float a, bool& tiny) {
     a = __builtin_fminf(a, 200.0f);         // e^{-200} is 0 in fp32; keeps the
                                             // products below finite
     const float p = -a * kLog2eHi;
     float perr = __builtin_fmaf(-a, kLog2eHi, -p);      // exact product error
     perr = __builtin_fmaf(-a, kLog2eLo, perr);
-    const bool tiny = p < -126.0f;
-    float r = __builtin_amdgcn_exp2f(tiny ? p + 64.0f : p);
-    r = __builtin_fmaf(r, perr * kLn2, r);
-    return tiny ? r * 0x1p-64f : r;
+    tiny = p < -126.0f;
+    const float r = __builtin_amdgcn_exp2f(tiny ? p + 64.0f : p);
+    return __builtin_fmaf(r, perr * kLn2, r);
 }
 
 // sigma(g) and 1 - sigma(g) without cancellation and without forming inf:
 // with e = e^{-|g|} and d = 1/(1+e) = sigma(|g|), sigma(g) is d for g >= 0 and
 // e*d otherwise, and 1 - sigma(g) = sigma(-g) is the other one.
-__device__ __forceinline__ void sigmoid_accurate(float g, float& sig, float& osig) {
-    const float e = exp_neg(__builtin_fabsf(g));
-    const float d = __builtin_amdgcn_rcpf(1.0f + e);
+// sigma(g) comes back times 1/scl: for g below about -87.3, where e^g is
+// under the normal range, sigma is kept as sigma 2^64 (a normal number with
+// all 24 bits) and scl = 2^-64, so that each output formed from it is
+// scaled back by one final multiply -- exact when the output is normal, a
+// single rounding when it is subnormal. Elsewhere scl = 1.
+__device__ __forceinline__ void sigmoid_accurate(float g, float& sig, float& osig, float& scl) {
+    bool tiny;
+    const float e = exp_neg_scaled(__builtin_fabsf(g), tiny);   // e^{-|g|} (x 2^64 if tiny)
+    const float d = __builtin_amdgcn_rcpf(1.0f + (tiny ? 0.0f : e));
     const float ed = e * d;
     const bool pos = g >= 0.0f;
     sig = pos ? d : ed;
-    osig = pos ? ed : d;
+    osig = pos ? (tiny ? ed * 0x1p-64f : ed) : d;
+    scl = !pos && tiny ? 0x1p-64f : 1.0f;
 }
 
 // h(g) = 1 + g (1 - sigma(g)), the factor with silu'(g) = sigma(g) h(g).
@@ -201,11 +208,17 @@ __device__ __forceinline__ float h_root_series(float g, float glo, float osig) {
 // Per-dtype choice. bf16 needs 2 ulp of an 8-bit significand: the bracket
 // 1 + g(1 - sigma) never comes closer to 0 than 0.0028 on the bf16 grid, so
 // the direct sum (absolute error ~1e-7) is far inside that. fp32 needs 1e-5
-// relative everywhere, including next to g0.
+// relative everywhere, including next to g0 and where sigma(g) is below the
+// normal range. Every output that sigma enters is multiplied by scl last
+// (1 for bf16, where the multiply folds away; see sigmoid_accurate).
 template <typename T, bool WANT_OSIG>
-__device__ __forceinline__ void sigmoid_pair(float g, float& sig, float& osig) {
-    if constexpr (sizeof(T) == 2) sigmoid_fast<WANT_OSIG>(g, sig, osig);
-    else sigmoid_accurate(g, sig, osig);
+__device__ __forceinline__ void sigmoid_pair(float g, float& sig, float& osig, float& scl) {
+    if constexpr (sizeof(T) == 2) {
+        sigmoid_fast<WANT_OSIG>(g, sig, osig);
+        scl = 1.0f;
+    } else {
+        sigmoid_accurate(g, sig, osig, scl);
+    }
 }
 
 template <typename T>

@@ -611,9 +611,9 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     const int64_t tw = t0 + c.wt, fw = f0 + c.wf;     // the wave's first token and feature
     epi_out(region, tw, fw, P.m, P.n, P.y, P.ldy, [&](int i, int j, int e) {
         const float g = acc.g[i][j][e];
-        float sig, osig;
-        sigmoid_pair<uint16_t, false>(g, sig, osig);
-        return (g * sig) * acc.u[i][j][e];
+        float sig, osig, scl;
+        sigmoid_pair<uint16_t, false>(g, sig, osig, scl);
+        return ((g * sig) * acc.u[i][j][e]) * scl;
     });
     if (P.x != nullptr) {
         epi_out(region, tw, fw, P.m, P.n, P.x, P.ldx,
@@ -640,9 +640,9 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
                 for (int r = 0; r < 4; ++r) {
                     gv[r] = acc.g[i][j][4 * q + r];
                     uv[r] = acc.u[i][j][4 * q + r];
-                    float sig, osig;
-                    sigmoid_pair<uint16_t, false>(gv[r], sig, osig);
-                    yv[r] = (gv[r] * sig) * uv[r];
+                    float sig, osig, scl;
+                    sigmoid_pair<uint16_t, false>(gv[r], sig, osig, scl);
+                    yv[r] = ((gv[r] * sig) * uv[r]) * scl;
                 }
                 store4(P.y + tok * P.ldy + f, yv);
                 if (P.x != nullptr) {

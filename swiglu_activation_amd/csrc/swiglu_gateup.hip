@@ -56,9 +56,9 @@ __global__ __launch_bounds__(kBlock) void swiglu_fwd_kernel(
     Vec<T, VEC>::load(up + row * us + c, u);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-        float sig, osig;
-        sigmoid_pair<T, false>(g[i], sig, osig);
-        out[i] = (g[i] * sig) * u[i];
+        float sig, osig, scl;
+        sigmoid_pair<T, false>(g[i], sig, osig, scl);
+        out[i] = ((g[i] * sig) * u[i]) * scl;
     }
     Vec<T, VEC>::store(y + row * ys + c, out);
 }
@@ -85,11 +85,13 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd_kernel(
     Vec<T, VEC>::load(dyp + row * dys + c, d);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-        float sig, osig;
-        sigmoid_pair<T, true>(g[i], sig, osig);
+        float sig, osig, scl;
+        sigmoid_pair<T, true>(g[i], sig, osig, scl);
         const float h = h_factor<T>(g[i], osig);
-        du[i] = d[i] * (g[i] * sig);
-        dg[i] = ((d[i] * u[i]) * sig) * h;
+        // sigma h = silu'(g) is at most 1.1 in magnitude, so forming it first
+        // leaves only the last multiply to round into the subnormal range
+        du[i] = (d[i] * (g[i] * sig)) * scl;
+        dg[i] = ((d[i] * u[i]) * (sig * h)) * scl;
     }
     Vec<T, VEC>::store(dgp + row * dgs + c, dg);
     Vec<T, VEC>::store(dup + row * dus + c, du);

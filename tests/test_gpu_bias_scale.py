@@ -278,3 +278,47 @@ def test_tile_and_row_loop_give_the_same_dx(dtype):
     for db, ds, what in ((db_t, ds_t, "tile"), (db_l, ds_l, "row loop")):
         _check_sum(db, db_ref, db_abs, f"dbias ({what})")
         _check_sum(ds, ds_ref, ds_abs, f"dscale ({what})")
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_fp32_gates_below_the_normal_range_of_sigma(in_place):
+    """fp32, biased gates z in [-100, -84]: sigma(z) ~ e^z is an fp32 subnormal
+    below z ~ -87.3 while silu(z) u stays normal down to z ~ -91.8. Every
+    output whose reference is a normal fp32 number meets the 1e-5 relative
+    bar, every subnormal one meets it up to one subnormal step (|got - ref| <=
+    1e-5 |ref| + 2^-149: the one rounding into the subnormal range), and
+    dbias and dscale meet their bars."""
+    print(f"[bias/scale fp32 low gates] in_place={in_place}", flush=True)
+    rng = np.random.default_rng(51)
+    rows, n = 128, 1024
+    bias = rng.uniform(-1.0, 1.0, 2 * n)
+    g = rng.uniform(-100.0, -84.0, (rows, n)) - bias[:n]
+    u = rng.choice([-1.0, 1.0], (rows, n)) * rng.uniform(1.0, 2.0, (rows, n))
+    dy = rng.choice([-1.0, 1.0], (rows, n)) * rng.uniform(1.0, 2.0, (rows, n))
+    x_h = np.concatenate([g, u], 1).astype(np.float32)
+    dy_h = dy.astype(np.float32)
+    b_h = bias.astype(np.float32)
+    s_h = rng.uniform(0.5, 1.0, rows).astype(np.float32)
+    y_ref, dx_ref, db_ref, ds_ref, db_abs, ds_abs = _refs(x_h, dy_h, b_h, s_h, "fp32")
+    x, dyt = gu.to_dev(x_h, "fp32"), gu.to_dev(dy_h, "fp32")
+    b, s = gu.to_dev(b_h, "fp32"), torch.from_numpy(s_h).cuda()
+    y = sw.swiglu_gateup_bias_scale_fwd(x, b, s)
+    dx, db, ds = sw.swiglu_gateup_bias_scale_bwd(dyt, x.clone() if in_place else x, b, s,
+                                                 in_place=in_place)
+    torch.cuda.synchronize()
+    tiny = 2.0 ** -126
+    counts = {}
+    for got_t, ref, what in ((y, y_ref, "fwd"), (dx, dx_ref, "dx")):
+        got = gu.from_dev(got_t).reshape(ref.shape).astype(np.float64)
+        normal = np.abs(ref) >= tiny
+        rel = np.abs(got - ref)[normal] / np.abs(ref[normal])
+        sub = ~normal & (ref != 0)
+        over = (np.abs(got - ref)[sub] - 1e-5 * np.abs(ref[sub])) / 2.0 ** -149
+        counts[what] = (int(normal.sum()), int(sub.sum()))
+        print(f"    {what}: {normal.sum()} normal (max rel {rel.max():.3g}), {sub.sum()} subnormal "
+              f"(max excess over 1e-5 |ref|: {over.max() if over.size else 0:.3g} steps)", flush=True)
+        assert rel.max() <= 1e-5 and (over.size == 0 or over.max() <= 1.0), what
+        assert np.all(got[ref == 0] == 0)
+    assert counts["fwd"][0] > 0 and counts["fwd"][1] > 0
+    _check_sum(db, db_ref, db_abs, "dbias")
+    _check_sum(ds, ds_ref, ds_abs, "dscale")
