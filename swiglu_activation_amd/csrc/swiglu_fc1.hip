@@ -35,11 +35,11 @@
 //  * The next k step's fragments are read while the current step's MFMAs
 //    run; one barrier per tile hands a filled stage to the readers and an
 //    emptied one to the copies.
-//  * A tile's copies are spread thinly over one k step each (token copies
-//    over the last step of the tile before, weight copies over the first
-//    step of the tile), not issued in a burst: a burst fills the copy queue,
-//    and the wave, which issues in order, then stalls in front of its next
-//    MFMA.
+//  * A tile's copies are spread evenly over the k steps, four per step
+//    (half of the next slot's token copies in step 0, the weight copies in
+//    steps 1 and 2, half of the token copies after the barrier), not issued
+//    in a burst: a burst fills the copy queue, and the wave, which issues in
+//    order, then stalls in front of its next MFMA.
 //    Each copy is addressed as a wave-uniform base in scalar registers plus
 //    a fixed 32-bit lane offset, so no vector instruction sits between two
 //    copies (which limits lda and ldw to 2^28 elements).
@@ -91,6 +91,9 @@ constexpr int kFcMF = kFcWaveF / 32;                 // ... along features (each
 constexpr int kFcTileT = kFcWaveT * kFcWavesT;       // tokens per workgroup
 constexpr int kFcTileF = kFcWaveF * kFcWavesF;       // features per workgroup
 constexpr int kFcTileK = 64;                         // k per stage
+#ifndef SWIGLU_FC_SPLIT
+#define SWIGLU_FC_SPLIT 4       // copy issue: 1 token and weight groups in one step each; 2 in halves
+#endif                          // over two steps each; 4 one half-group in every step
 #ifndef SWIGLU_FC_A_STAGES
 #define SWIGLU_FC_A_STAGES 2    // LDS stages of token rows
 #endif
@@ -503,6 +506,50 @@ __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F
     constexpr int SA = J % kFcAStages, SW = J % kFcWStages;
     constexpr int SWP = (J + kFcPeriod - 1) % kFcWStages;     // tile kt - 1's weight stage
     constexpr int SAN = (J + 1) % kFcAStages, SWN = (J + 1) % kFcWStages;
+#if SWIGLU_FC_SPLIT == 4
+    // one copy group per step: the second half of slot kt + 1's token
+    // copies, the weight copies of slot kt - 1 + W_STAGES in two halves,
+    // and after the barrier the first half of slot kt + 2's token copies
+    constexpr int SAP = (J + kFcPeriod - 1) % kFcAStages;     // tile kt - 1's token stage
+    constexpr int HA = kFcCopiesA / 2, HW = kFcCopiesW / 2;
+    copy_a<SAP, HA, kFcCopiesA>(c.src, source_tile(c, kt + 1));
+    load_frags<SA, SW>(c.wt, c.wf, c.off[1], F1);
+    mfma_step(F0, acc);
+    sched_mix_at<kFcCopiesA - HA>();
+    copy_w<SWP, 0, HW>(c.src, source_tile(c, kt - 1 + kFcWStages));
+    load_frags<SA, SW>(c.wt, c.wf, c.off[2], F0);
+    mfma_step(F1, acc);
+    sched_mix_at<HW>();
+    copy_w<SWP, HW, kFcCopiesW>(c.src, source_tile(c, kt - 1 + kFcWStages));
+    load_frags<SA, SW>(c.wt, c.wf, c.off[3], F1);
+    mfma_step(F0, acc);
+    sched_mix_at<kFcCopiesW - HW>();
+    wait_copies_and_lds<kWaitSlot>();
+    ring_barrier();
+    copy_a<SA, 0, HA>(c.src, source_tile(c, kt + kFcAStages));
+    load_frags<SAN, SWN>(c.wt, c.wf, c.off[0], F0);
+    mfma_step(F1, acc);
+    sched_mix_at<HA>();
+#elif SWIGLU_FC_SPLIT == 2
+    constexpr int SAP = (J + kFcPeriod - 1) % kFcAStages;     // tile kt - 1's token stage
+    constexpr int HA = kFcCopiesA / 2, HW = kFcCopiesW / 2;
+    copy_a<SAP, HA, kFcCopiesA>(c.src, source_tile(c, kt + 1));
+    copy_w<SWP, 0, HW>(c.src, source_tile(c, kt - 1 + kFcWStages));
+    load_frags<SA, SW>(c.wt, c.wf, c.off[1], F1);
+    mfma_step(F0, acc);
+    sched_mix_at<kFcCopiesA - HA + HW>();
+    copy_w<SWP, HW, kFcCopiesW>(c.src, source_tile(c, kt - 1 + kFcWStages));
+    load_frags<SA, SW>(c.wt, c.wf, c.off[2], F0);
+    mfma_step(F1, acc);
+    sched_mix_at<kFcCopiesW - HW>();
+    inner_step<SA, SW, 2>(c, F0, F1, acc);
+    wait_copies_and_lds<kWaitSlot>();
+    ring_barrier();
+    copy_a<SA, 0, HA>(c.src, source_tile(c, kt + kFcAStages));
+    load_frags<SAN, SWN>(c.wt, c.wf, c.off[0], F0);
+    mfma_step(F1, acc);
+    sched_mix_at<HA>();
+#else
     copy_w<SWP>(c.src, source_tile(c, kt - 1 + kFcWStages));
     load_frags<SA, SW>(c.wt, c.wf, c.off[1], F1);
     mfma_step(F0, acc);
@@ -515,6 +562,7 @@ __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F
     load_frags<SAN, SWN>(c.wt, c.wf, c.off[0], F0);
     mfma_step(F1, acc);
     sched_mix_at<kFcCopiesA>();
+#endif
 }
 
 // A whole period of slots from kt (a multiple of the period).
@@ -548,9 +596,16 @@ template <int P>
 __device__ __forceinline__ void prologue(const Ctx& c, Frags& F0) {
     copy_a<P % kFcAStages>(c.src, source_tile(c, P));
     copy_w<P % kFcWStages>(c.src, source_tile(c, P));
+#if SWIGLU_FC_SPLIT >= 2
+    // the second half of slot P + 1's token copies is issued by tile P
+    copy_a<(P + 1) % kFcAStages, 0, kFcCopiesA / 2>(c.src, source_tile(c, P + 1));
+    if constexpr (kFcWStages == 3) copy_w<(P + 1) % kFcWStages>(c.src, source_tile(c, P + 1));
+    wait_copies_and_lds<kFcCopiesA / 2 + (kFcWStages == 3 ? kFcCopiesW : 0)>();
+#else
     copy_a<(P + 1) % kFcAStages>(c.src, source_tile(c, P + 1));
     if constexpr (kFcWStages == 3) copy_w<(P + 1) % kFcWStages>(c.src, source_tile(c, P + 1));
     wait_copies_and_lds<kFcCopiesA + (kFcWStages == 3 ? kFcCopiesW : 0)>();
+#endif
     ring_barrier();
     load_frags<P % kFcAStages, P % kFcWStages>(c.wt, c.wf, c.off[0], F0);
 }
