@@ -72,7 +72,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define SWIGLU_FC_CPOL 0        // cache-policy bits of the copies (gfx950: 1 sc0, 2 nt)
 #endif
 #ifndef SWIGLU_FC_SCHED
-#define SWIGLU_FC_SCHED 1       // pin the interleaving of MFMAs and memory instructions
+#define SWIGLU_FC_SCHED 2       // 2: a fixed instruction order per step; 1: pinned interleaving hints
 #endif
 #ifndef SWIGLU_FC_SADDR
 #define SWIGLU_FC_SADDR 1       // copies as a wave-uniform base (SGPRs) plus a fixed 32-bit lane offset
@@ -477,6 +477,56 @@ __device__ __forceinline__ int source_tile(const Ctx& c, int kt) {
     return t < 0 ? 0 : t < c.kt_count ? t : c.kt_count - 1;
 }
 
+#ifndef SWIGLU_FC_COPY_POS
+#define SWIGLU_FC_COPY_POS 9    // strict schedule: MFMA index after which a step's first copy goes
+#endif
+#ifndef SWIGLU_FC_COPY_STRIDE
+#define SWIGLU_FC_COPY_STRIDE 2 // ... and the MFMAs between two copies
+#endif
+#ifndef SWIGLU_FC_COPY_POS0
+#define SWIGLU_FC_COPY_POS0 SWIGLU_FC_COPY_POS   // ... for step 0's copies
+#endif
+#ifndef SWIGLU_FC_COPY_POS3
+#define SWIGLU_FC_COPY_POS3 1   // SPLIT 3: positions of the token copies after the barrier
+#endif
+#ifndef SWIGLU_FC_COPY_STRIDE3
+#define SWIGLU_FC_COPY_STRIDE3 2
+#endif
+#ifndef SWIGLU_FC_READ_STRIDE
+#define SWIGLU_FC_READ_STRIDE 1 // strict schedule: MFMAs between two fragment reads (from MFMA 0)
+#endif
+
+// One k step in a fixed instruction order (SWIGLU_FC_SCHED 2): MFMA m of
+// the step (the order of mfma_step), then, at their positions, one fragment
+// read of the next step into N and one copy (copy(q) issues the step's copy
+// q), with a scheduling barrier after every group so that nothing moves.
+template <int SA, int SW, int NC, int POS, int STRIDE, class CopyFn>
+__device__ __forceinline__ void step_strict(const Ctx& c, int off, const Frags& C, Frags& N,
+                                            Acc& acc, CopyFn copy) {
+    static_assert(NC == 0 || POS + (NC - 1) * STRIDE < kFcMfma,
+                  "every copy of the step has an MFMA to follow");
+    static_assert((kFcReads - 1) * SWIGLU_FC_READ_STRIDE < kFcMfma, "every read has an MFMA to follow");
+    const uint16_t* ta = stage_a<SA>();
+    const uint16_t* tw = stage_w<SW>();
+#pragma unroll
+    for (int m = 0; m < kFcMfma; ++m) {
+        const int i = m / (2 * kFcMT), j = (m / 2) % kFcMT;
+        if (m & 1)
+            acc.u[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(C.u[i], C.a[j], acc.u[i][j], 0, 0, 0);
+        else
+            acc.g[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(C.g[i], C.a[j], acc.g[i][j], 0, 0, 0);
+        if (m % SWIGLU_FC_READ_STRIDE == 0 && m / SWIGLU_FC_READ_STRIDE < kFcReads) {
+            const int r = m / SWIGLU_FC_READ_STRIDE;
+            if (r < kFcMT) N.a[r] = frag(ta + (c.wt + 32 * r) * kFcRowElems + off);
+            else if (r < kFcMT + kFcMF) N.g[r - kFcMT] = frag(tw + (c.wf + 32 * (r - kFcMT)) * kFcRowElems + off);
+            else N.u[r - kFcMT - kFcMF] =
+                     frag(tw + (kFcTileF + c.wf + 32 * (r - kFcMT - kFcMF)) * kFcRowElems + off);
+        }
+        if (m >= POS && (m - POS) % STRIDE == 0 && (m - POS) / STRIDE < NC) copy((m - POS) / STRIDE);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // One k step of tile (SA, SW) with fragments C while the next step's are
 // read into N.
 template <int SA, int SW, int STEP>
@@ -506,7 +556,52 @@ __device__ __forceinline__ void k_tile(const Ctx& c, int kt, Frags& F0, Frags& F
     constexpr int SA = J % kFcAStages, SW = J % kFcWStages;
     constexpr int SWP = (J + kFcPeriod - 1) % kFcWStages;     // tile kt - 1's weight stage
     constexpr int SAN = (J + 1) % kFcAStages, SWN = (J + 1) % kFcWStages;
+#if SWIGLU_FC_SCHED == 2
+    constexpr int SAP = (J + kFcPeriod - 1) % kFcAStages;     // tile kt - 1's token stage
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ta1 = source_tile(c, kt + 1), tw2 = source_tile(c, kt - 1 + kFcWStages);
+    const int ta2 = source_tile(c, kt + kFcAStages);
+    auto blk_a = [&](int i) { return copy_block(i, wave) * kFcCopyRows * kFcRowElems; };
+    auto blk_w = [&](int j) {
+        return (copy_block(kFcCopiesA + j, wave) - kFcRowsA / kFcCopyRows) * kFcCopyRows * kFcRowElems;
+    };
+    constexpr int P = SWIGLU_FC_COPY_POS, S = SWIGLU_FC_COPY_STRIDE;
 #if SWIGLU_FC_SPLIT == 4
+    constexpr int HA = kFcCopiesA / 2, HW = kFcCopiesW / 2;
+    step_strict<SA, SW, HA, SWIGLU_FC_COPY_POS0, S>(c, c.off[1], F0, F1, acc, [&](int q) {
+        copy_one(c.src, HA + q, ta1, stage_a<SAP>() + blk_a(HA + q));
+    });
+    step_strict<SA, SW, HW, P, S>(c, c.off[2], F1, F0, acc, [&](int q) {
+        copy_one(c.src, kFcCopiesA + q, tw2, stage_w<SWP>() + blk_w(q));
+    });
+    step_strict<SA, SW, kFcCopiesW - HW, P, S>(c, c.off[3], F0, F1, acc, [&](int q) {
+        copy_one(c.src, kFcCopiesA + HW + q, tw2, stage_w<SWP>() + blk_w(HW + q));
+    });
+    wait_copies_and_lds<kWaitSlot>();
+    ring_barrier();
+    step_strict<SAN, SWN, HA, P, S>(c, c.off[0], F1, F0, acc, [&](int q) {
+        copy_one(c.src, q, ta2, stage_a<SA>() + blk_a(q));
+    });
+#elif SWIGLU_FC_SPLIT == 3
+    // the weight copies over steps 0-2, all token copies after the barrier
+    constexpr int W0 = (kFcCopiesW + 2) / 3, W1 = (kFcCopiesW + 1) / 3;
+    step_strict<SA, SW, W0, P, S>(c, c.off[1], F0, F1, acc, [&](int q) {
+        copy_one(c.src, kFcCopiesA + q, tw2, stage_w<SWP>() + blk_w(q));
+    });
+    step_strict<SA, SW, W1, P, S>(c, c.off[2], F1, F0, acc, [&](int q) {
+        copy_one(c.src, kFcCopiesA + W0 + q, tw2, stage_w<SWP>() + blk_w(W0 + q));
+    });
+    step_strict<SA, SW, kFcCopiesW - W0 - W1, P, S>(c, c.off[3], F0, F1, acc, [&](int q) {
+        copy_one(c.src, kFcCopiesA + W0 + W1 + q, tw2, stage_w<SWP>() + blk_w(W0 + W1 + q));
+    });
+    wait_copies_and_lds<kWaitSlot>();
+    ring_barrier();
+    step_strict<SAN, SWN, kFcCopiesA, SWIGLU_FC_COPY_POS3, SWIGLU_FC_COPY_STRIDE3>(
+        c, c.off[0], F1, F0, acc, [&](int q) { copy_one(c.src, q, ta2, stage_a<SA>() + blk_a(q)); });
+#else
+#error "the strict schedule takes SWIGLU_FC_SPLIT 3 or 4"
+#endif
+#elif SWIGLU_FC_SPLIT == 4
     // one copy group per step: the second half of slot kt + 1's token
     // copies, the weight copies of slot kt - 1 + W_STAGES in two halves,
     // and after the barrier the first half of slot kt + 2's token copies
@@ -596,7 +691,7 @@ template <int P>
 __device__ __forceinline__ void prologue(const Ctx& c, Frags& F0) {
     copy_a<P % kFcAStages>(c.src, source_tile(c, P));
     copy_w<P % kFcWStages>(c.src, source_tile(c, P));
-#if SWIGLU_FC_SPLIT >= 2
+#if SWIGLU_FC_SPLIT == 2 || SWIGLU_FC_SPLIT == 4
     // the second half of slot P + 1's token copies is issued by tile P
     copy_a<(P + 1) % kFcAStages, 0, kFcCopiesA / 2>(c.src, source_tile(c, P + 1));
     if constexpr (kFcWStages == 3) copy_w<(P + 1) % kFcWStages>(c.src, source_tile(c, P + 1));
