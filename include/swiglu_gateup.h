@@ -297,20 +297,34 @@ swiglu_status swiglu_gateup_bias_scale_bwd_noalloc(const void* dy, int64_t dy_ro
  *   m, n, k       sizes: m >= 0; n a multiple of 64 in [0, 2^30]; k a
  *                 positive multiple of 64 (k may be 0 only when m or n is 0).
  *   dtype         must be SWIGLU_DTYPE_BF16.
+ *   workspace     NULL, or swiglu_fc1_workspace_size() bytes of device memory,
+ *                 owned by the caller, that are all zero on entry. With it,
+ *                 the kernel runs one workgroup per CU, and the workgroups
+ *                 share the output tiles through counters kept there. Tiles
+ *                 then go to whichever XCD is free, instead of a fixed share
+ *                 each. The call leaves the workspace all zero again once it
+ *                 completes, so one workspace serves every call on one
+ *                 stream. Calls that use the same workspace must not overlap
+ *                 in time (e.g. on two streams). With NULL, each tile is its
+ *                 own workgroup. y and x_out are the same bits either way.
+ *   stream        HIP stream of the launch.
  * All pointers must be 16-byte aligned and all row strides multiples of 8;
  * lda and ldw (hence k) are at most 2^28 elements.
  *
  * Errors: SWIGLU_ERR_BAD_DTYPE (not bf16), SWIGLU_ERR_BAD_SHAPE (n or k not
  * multiples of 64, k == 0 with a non-empty output), SWIGLU_ERR_BAD_STRIDE
- * (strides below the widths or lda / ldw above 2^28, misaligned pointers
- * or strides),
+ * (strides below the widths or lda / ldw above 2^28, misaligned pointers,
+ * workspace or strides),
  * SWIGLU_ERR_NULL_POINTER, SWIGLU_ERR_ALIASING (an output overlaps an input
- * or the other output), SWIGLU_ERR_HIP.
+ * or the other output, or the workspace overlaps any of them), SWIGLU_ERR_HIP.
  */
 swiglu_status swiglu_fc1_fwd(const void* a, int64_t lda, const void* w, int64_t ldw,
                              void* y, int64_t ldy, void* x_out, int64_t ldx,
                              int64_t m, int64_t n, int64_t k,
-                             swiglu_dtype dtype, hipStream_t stream);
+                             swiglu_dtype dtype, void* workspace, hipStream_t stream);
+
+/* Bytes of the workspace that swiglu_fc1_fwd takes (a constant). */
+size_t swiglu_fc1_workspace_size(void);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* swiglu_status_string(swiglu_status status);

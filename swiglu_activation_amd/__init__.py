@@ -19,7 +19,8 @@ import os
 __all__ = ["swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
            "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
            "swiglu_gateup_bias_scale_workspace_size", "swiglu_gateup_bias_scale_bwd_noalloc",
-           "swiglu_fc1_fwd", "swiglu_status_string", "SwiGLUError", "library_path",
+           "swiglu_fc1_fwd", "swiglu_fc1_workspace_size", "swiglu_status_string", "SwiGLUError",
+           "library_path",
            "load_library", "EXPORTS", "NOALLOC_SCRATCH_BYTES"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +44,7 @@ _BAD_DTYPE_CODE = -1    # passed for any other torch dtype; the library rejects 
 EXPORTS = ("swiglu_gateup_fwd", "swiglu_gateup_bwd", "swiglu_silu_mul_fwd", "swiglu_silu_mul_bwd",
            "swiglu_gateup_bias_scale_fwd", "swiglu_gateup_bias_scale_bwd",
            "swiglu_gateup_bias_scale_workspace_size", "swiglu_gateup_bias_scale_bwd_noalloc",
-           "swiglu_fc1_fwd", "swiglu_status_string")
+           "swiglu_fc1_fwd", "swiglu_fc1_workspace_size", "swiglu_status_string")
 
 _lib = None
 
@@ -94,8 +95,10 @@ def load_library():
     lib.swiglu_gateup_bias_scale_bwd_noalloc.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64,
                                                          vp, vp, i64, i64, i64, cint, cint, vp]
     lib.swiglu_gateup_bias_scale_bwd_noalloc.restype = cint
-    lib.swiglu_fc1_fwd.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, cint, vp]
+    lib.swiglu_fc1_fwd.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, cint, vp, vp]
     lib.swiglu_fc1_fwd.restype = cint
+    lib.swiglu_fc1_workspace_size.argtypes = []
+    lib.swiglu_fc1_workspace_size.restype = ctypes.c_size_t
     lib.swiglu_status_string.argtypes = [cint]
     lib.swiglu_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -484,14 +487,45 @@ def swiglu_gateup_bias_scale_bwd_noalloc(dy, x, dx=None, dbias=None, dscale=None
 # fc1 projection with the SwiGLU epilogue
 # ---------------------------------------------------------------------------
 
-def swiglu_fc1_fwd(a, w, y=None, *, x_out=None, stream=None):
+def swiglu_fc1_workspace_size() -> int:
+    return int(load_library().swiglu_fc1_workspace_size())
+
+
+# One zeroed fc1 workspace per (device, stream): the kernel leaves it zeroed,
+# and launches on one stream never overlap.
+_fc1_workspaces: dict = {}
+
+
+def _fc1_workspace(device, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    if torch.cuda.is_current_stream_capturing():
+        # memory allocated under capture belongs to the graph's pool: the
+        # captured launch uses one workgroup per tile instead
+        return None
+    key = (torch.device(device).index, s.cuda_stream)
+    ws = _fc1_workspaces.get(key)
+    if ws is None:
+        with torch.cuda.stream(s):
+            ws = torch.zeros(swiglu_fc1_workspace_size(), dtype=torch.uint8, device=device)
+        _fc1_workspaces[key] = ws
+    return ws
+
+
+def swiglu_fc1_fwd(a, w, y=None, *, x_out=None, stream=None, workspace=None):
     """y = silu(a @ w[:n].T) * (a @ w[n:].T) for bf16 a [..., k] and w [2n, k].
 
     x_out: None, True (allocate) or a [..., 2n] tensor that receives a @ w.T.
     Returns y, or (y, x_out) when x_out is requested. n and k must be
     multiples of 64, rows 16-byte aligned, and the row strides of a and w at
     most 2^28 elements; anything else raises ValueError (the C entry point's
-    status)."""
+    status).
+
+    workspace: None (a zeroed buffer kept per device and stream; none while
+    the stream is being captured into a graph), False (none: one workgroup
+    per tile), or a device tensor of swiglu_fc1_workspace_size() bytes that
+    is all zero and not in use by another launch. The outputs are the same
+    bits either way."""
     import torch
     lib = load_library()
     _require_device(a, w, y, x_out if isinstance(x_out, torch.Tensor) else None)
@@ -518,8 +552,18 @@ def swiglu_fc1_fwd(a, w, y=None, *, x_out=None, stream=None):
             raise ValueError("x_out must be bfloat16")
         ldx = _same_rows(x_out, m, 2 * n, "x_out")
         xp = x_out.data_ptr()
+    if workspace is None:
+        workspace = _fc1_workspace(a.device, stream)
+    elif workspace is False:
+        workspace = None
+    wsp = None
+    if workspace is not None:
+        _require_device(workspace, a)
+        if workspace.numel() * workspace.element_size() < swiglu_fc1_workspace_size():
+            raise ValueError("fc1 workspace smaller than swiglu_fc1_workspace_size()")
+        wsp = workspace.data_ptr()
     with torch.cuda.device(a.device):
         st = lib.swiglu_fc1_fwd(a.data_ptr(), lda, w.data_ptr(), ldw, y.data_ptr(), ldy, xp, ldx,
-                                m, n, k, _dtype_code(a), _stream_handle(a.device, stream))
+                                m, n, k, _dtype_code(a), wsp, _stream_handle(a.device, stream))
     _check(st, "swiglu_fc1_fwd")
     return (y, x_out) if want_x else y

@@ -115,6 +115,28 @@ inline int64_t fc1_rows_per_launch(int64_t n, int64_t tile_f, int64_t tile_t, in
     return t * tile_t;
 }
 
+// fc1 launch with a tile pool: the first n_fixed of `tiles` tiles go one per
+// workgroup, the rest form the pool, and the grid holds `grid` workgroups
+// (grid - n_fixed of them take from the pool: a quarter more than its
+// tiles). Only launches of at least 16 tiles per CU get a pool (cus <= 0:
+// none); n_fixed is a multiple of 8 (the pool starts on a whole round of the
+// 8 XCDs), and the grid's work-item count stays below 2^32, the surplus
+// shrinking first.
+struct Fc1Pool {
+    uint32_t n_fixed, grid;
+};
+
+inline Fc1Pool fc1_pool(uint32_t tiles, int64_t cus, int64_t threads) {
+    if (cus <= 0 || (int64_t)tiles < 16 * cus) return {tiles, tiles};
+    const uint32_t n_fixed = tiles / 8 * 8 - tiles / 4 / 8 * 8;   // about three quarters
+    const uint32_t pool = tiles - n_fixed;
+    const int64_t max_wg = (((int64_t)1 << 32) - 1) / threads;
+    int64_t grid = (int64_t)tiles + (pool + 3) / 4;
+    if (grid > max_wg) grid = max_wg;
+    if (grid <= (int64_t)tiles) return {tiles, tiles};
+    return {n_fixed, (uint32_t)grid};
+}
+
 }  // namespace swiglu_host
 
 #endif  // SWIGLU_HOST_LOGIC_H

@@ -705,11 +705,59 @@ __device__ __forceinline__ void prologue(const Ctx& c, Frags& F0) {
     load_frags<P % kFcAStages, P % kFcWStages>(c.wt, c.wf, c.off[0], F0);
 }
 
-__global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint32_t f_tiles,
-                                                                uint32_t t_tiles) {
+// Dynamic tail. Under full load the XCDs run at clocks several percent
+// apart, and the hardware deals the workgroups to them in turn, a fixed share
+// each, so the fastest XCD idles while the slowest finishes. With a
+// workspace, the first tiles of the launch order still go one per workgroup
+// (tile blockIdx.x), but the last tiles form a pool that later workgroups
+// take from as they start: those run wherever an XCD has room, so the faster
+// XCDs take more of them. The grid holds more pool workgroups than pool
+// tiles (the surplus finds the pool empty and ends at once).
+// The pool is split into 8 queues, one per XCD, in the order the hardware
+// would deal its tiles (pool tile p to queue p % 8); a workgroup takes from
+// the queue of the XCD it runs on, so the tiles that an L2 serves at one
+// time stay those of one workgroup per tile, and from the other queues once
+// its own is empty. The workspace holds the 8 queue counters and a count of
+// the pool workgroups that have taken their tile; the last of them sets all
+// nine back to zero.
+constexpr uint32_t kFcQueues = 8;
+constexpr uint32_t kFcQueueStride = 32;            // 32-bit words between counters (128 bytes)
+constexpr uint32_t kFcDoneWord = kFcQueues * kFcQueueStride;
+constexpr size_t kFcWorkspaceBytes = (kFcQueues + 1) * kFcQueueStride * 4;
+
+__device__ __forceinline__ uint32_t queue_len(uint32_t pool, uint32_t q) {
+    return pool > q ? (pool - 1 - q) / kFcQueues + 1 : 0;
+}
+
+__device__ __forceinline__ uint32_t fetch_add_agent(uint32_t* p) {
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A pool tile (in [0, pool)) for a workgroup on XCD home: from its own queue,
+// else from the first other queue that still has one; pool if none is left.
+// A queue once found empty stays empty (its counter only grows).
+__device__ uint32_t take_pool_tile(uint32_t* ws, uint32_t home, uint32_t pool) {
+    for (uint32_t s = 0; s < kFcQueues; ++s) {
+        const uint32_t q = (home + s) % kFcQueues;
+        const uint32_t len = queue_len(pool, q);
+        if (len == 0) continue;
+        const uint32_t j = fetch_add_agent(ws + q * kFcQueueStride);
+        if (j < len) return q + kFcQueues * j;
+    }
+    return pool;
+}
+
+// The XCD this wave runs on (hardware register XCC_ID, bits [3:0]).
+__device__ __forceinline__ uint32_t xcd_id() {
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) % kFcQueues;
+}
+
+// Output tile b of the launch order: 256 tokens x 128 features of y.
+__device__ __forceinline__ void fc1_tile(const Fc1Args& P, uint32_t b, uint32_t f_tiles,
+                                         uint32_t t_tiles) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t ft, tt;
-    tile_of(blockIdx.x, f_tiles, t_tiles, ft, tt);
+    tile_of(b, f_tiles, t_tiles, ft, tt);
     const int64_t f0 = (int64_t)ft * kFcTileF;
     const int64_t t0 = (int64_t)tt * kFcTileT;
 
@@ -749,7 +797,7 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
     }
     first_pass(c, F0, F1, acc);
     for (int kt = kFcPeriod; kt < slots; kt += kFcPeriod) full_pass(c, kt, F0, F1, acc);
-    // No copy may still be writing LDS when the workgroup ends.
+    // No copy may still be writing LDS when the stages are reused.
     wait_copies_and_lds<0>();
 
 #if SWIGLU_FC_LDS_EPI
@@ -804,13 +852,56 @@ __global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint3
 #endif
 }
 
+// Workgroups below n_fixed compute tile blockIdx.x. The others (only with a
+// workspace) each take one tile of the pool [n_fixed, total) through the
+// queues in ws, which are all zero on entry and all zero again on exit.
+__global__ __launch_bounds__(kFcThreads) void swiglu_fc1_kernel(Fc1Args P, uint32_t f_tiles,
+                                                                uint32_t t_tiles, uint32_t* ws,
+                                                                uint32_t n_fixed) {
+    const uint32_t total = f_tiles * t_tiles;
+    uint32_t b = blockIdx.x;
+    if (b >= n_fixed) {
+        // Thread 0 takes the tile and hands it to every wave through LDS
+        // (stage memory, not yet in use).
+        uint32_t* word = reinterpret_cast<uint32_t*>(stage_a<0>());
+        if (threadIdx.x == 0) {
+            const uint32_t pool = total - n_fixed;
+            const uint32_t p = take_pool_tile(ws, xcd_id(), pool);
+            *word = n_fixed + p;
+            // Count this workgroup once its tile is taken. The last pool
+            // workgroup to be counted has seen every other one take its
+            // tile, so no counter is touched again in this launch: it
+            // clears them for the next launch on this workspace.
+            const uint32_t done = fetch_add_agent(ws + kFcDoneWord);
+            if (done == gridDim.x - n_fixed - 1) {
+                for (uint32_t q = 0; q <= kFcQueues; ++q)
+                    __hip_atomic_store(ws + q * kFcQueueStride, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        wait_copies_and_lds<63>();
+        ring_barrier();
+        b = __builtin_amdgcn_readfirstlane(*word);
+        // every wave has read the word before any copy can land on it
+        wait_copies_and_lds<63>();
+        ring_barrier();
+        if (b >= total) return;
+    }
+    fc1_tile(P, b, f_tiles, t_tiles);
+}
+
 }  // namespace
 
 extern "C" {
 
+__attribute__((visibility("default"))) size_t swiglu_fc1_workspace_size(void) {
+    return kFcWorkspaceBytes;
+}
+
 __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
     const void* a, int64_t lda, const void* w, int64_t ldw, void* y, int64_t ldy, void* x_out,
-    int64_t ldx, int64_t m, int64_t n, int64_t k, swiglu_dtype dtype, hipStream_t stream) {
+    int64_t ldx, int64_t m, int64_t n, int64_t k, swiglu_dtype dtype, void* workspace,
+    hipStream_t stream) {
     if (dtype != SWIGLU_DTYPE_BF16) return SWIGLU_ERR_BAD_DTYPE;
     // 2n weight rows and k fit in 31 bits, so the feature-tile count fits
     // one launch dimension with room to spare
@@ -845,6 +936,25 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
                                        swiglu_host::span_of(ow, 2 * n, k, 2)))
             return SWIGLU_ERR_ALIASING;
     }
+    if (workspace != nullptr) {
+        if ((uintptr_t)workspace % 16 != 0) return SWIGLU_ERR_BAD_STRIDE;
+        const swiglu_host::Span sw{(uintptr_t)workspace, (uintptr_t)workspace + kFcWorkspaceBytes};
+        if (swiglu_host::spans_overlap(sw, swiglu_host::span_of(oa, m, k, 2)) ||
+            swiglu_host::spans_overlap(sw, swiglu_host::span_of(ow, 2 * n, k, 2)) ||
+            swiglu_host::spans_overlap(sw, swiglu_host::span_of(oy, m, n, 2)) ||
+            (x_out != nullptr && swiglu_host::spans_overlap(sw, swiglu_host::span_of(ox, m, 2 * n, 2))))
+            return SWIGLU_ERR_ALIASING;
+    }
+    // With a workspace, launches of at least 16 tiles per CU end on a pool
+    // (a tile is one workgroup on one CU, whose LDS its stages fill).
+    int64_t cus = 0;
+    if (workspace != nullptr) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return SWIGLU_ERR_HIP;
+        cus = v;
+    }
 
     Fc1Args P;
     P.a = static_cast<const uint16_t*>(a);
@@ -862,8 +972,9 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
     const int64_t rows_per_launch =
         swiglu_host::fc1_rows_per_launch(n, kFcTileF, kFcTileT, kMaxGridY, kFcThreads);
     if (rows_per_launch <= 0) return SWIGLU_ERR_BAD_SHAPE;
-    uint32_t t_tiles = 0;
-    void* args[] = {&P, const_cast<uint32_t*>(&f_tiles), &t_tiles};
+    uint32_t t_tiles = 0, n_fixed = 0;
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
+    void* args[] = {&P, const_cast<uint32_t*>(&f_tiles), &t_tiles, &ws, &n_fixed};
     for (int64_t r0 = 0; r0 < m; r0 += rows_per_launch) {
         const int64_t mc = m - r0 < rows_per_launch ? m - r0 : rows_per_launch;
         P.a = static_cast<const uint16_t*>(a) + r0 * lda;
@@ -871,8 +982,12 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
         P.x = x_out ? static_cast<uint16_t*>(x_out) + r0 * ldx : nullptr;
         P.m = mc;
         t_tiles = (uint32_t)((mc + kFcTileT - 1) / kFcTileT);
-        if (hipLaunchKernel(reinterpret_cast<const void*>(&swiglu_fc1_kernel),
-                            dim3(f_tiles * t_tiles), dim3(kFcThreads), args, 0, stream) != hipSuccess)
+        const uint32_t tiles = f_tiles * t_tiles;
+        const swiglu_host::Fc1Pool pool = swiglu_host::fc1_pool(tiles, cus, kFcThreads);
+        n_fixed = pool.n_fixed;
+        const uint32_t grid = pool.grid;
+        if (hipLaunchKernel(reinterpret_cast<const void*>(&swiglu_fc1_kernel), dim3(grid),
+                            dim3(kFcThreads), args, 0, stream) != hipSuccess)
             return SWIGLU_ERR_HIP;
     }
     return SWIGLU_OK;

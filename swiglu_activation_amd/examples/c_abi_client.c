@@ -90,6 +90,21 @@ static void* dev_alloc(size_t bytes) {
     return d;
 }
 
+/* exits unless the two device buffers hold the same bytes */
+static void check_equal(const void* d1, const void* d2, size_t bytes, const char* what) {
+    unsigned char* h1 = (unsigned char*)malloc(bytes ? bytes : 1);
+    unsigned char* h2 = (unsigned char*)malloc(bytes ? bytes : 1);
+    if (!h1 || !h2) exit(1);
+    HIP_OK(hipMemcpy(h1, d1, bytes, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(h2, d2, bytes, hipMemcpyDeviceToHost));
+    if (memcmp(h1, h2, bytes) != 0) {
+        fprintf(stderr, "%s: outputs differ\n", what);
+        exit(1);
+    }
+    free(h1);
+    free(h2);
+}
+
 static void expect(swiglu_status got, swiglu_status want, const char* what) {
     if (got != want) {
         fprintf(stderr, "%s: got %s, want %s\n", what, swiglu_status_string(got),
@@ -198,16 +213,27 @@ static void run_fc1(char** a, hipStream_t st) {
     void* wd = upload(a[4], wb);
     void* y = dev_alloc(yb);
     void* xo = dev_alloc(xb);
-    expect(swiglu_fc1_fwd(ad, k, wd, k, y, n, NULL, 0, m, n, k, SWIGLU_DTYPE_F32, st),
+    void* y2 = dev_alloc(yb);
+    /* the tile-queue workspace: zeroed once, left zeroed by every call */
+    void* ws = dev_alloc(swiglu_fc1_workspace_size());
+    HIP_OK(hipMemsetAsync(ws, 0, swiglu_fc1_workspace_size(), st));
+    expect(swiglu_fc1_fwd(ad, k, wd, k, y, n, NULL, 0, m, n, k, SWIGLU_DTYPE_F32, NULL, st),
            SWIGLU_ERR_BAD_DTYPE, "fc1 in fp32");
-    SW_OK(swiglu_fc1_fwd(ad, k, wd, k, y, n, xo, 2 * n, m, n, k, SWIGLU_DTYPE_BF16, st));
+    expect(swiglu_fc1_fwd(ad, k, wd, k, y, n, NULL, 0, m, n, k, SWIGLU_DTYPE_BF16,
+                          (char*)ws + 8, st),
+           SWIGLU_ERR_BAD_STRIDE, "fc1 with a misaligned workspace");
+    SW_OK(swiglu_fc1_fwd(ad, k, wd, k, y, n, xo, 2 * n, m, n, k, SWIGLU_DTYPE_BF16, ws, st));
+    SW_OK(swiglu_fc1_fwd(ad, k, wd, k, y2, n, NULL, 0, m, n, k, SWIGLU_DTYPE_BF16, NULL, st));
     HIP_OK(hipStreamSynchronize(st));
+    check_equal(y, y2, yb, "fc1 with and without a workspace");
     download(a[5], y, yb);
     download(a[6], xo, xb);
     HIP_OK(hipFree(ad));
     HIP_OK(hipFree(wd));
     HIP_OK(hipFree(y));
+    HIP_OK(hipFree(y2));
     HIP_OK(hipFree(xo));
+    HIP_OK(hipFree(ws));
 }
 
 int main(int argc, char** argv) {

@@ -284,8 +284,8 @@ def test_noalloc_validation(lib):
     assert bsn(lib, None, 8, None, 16, None, None, 1, None, 16, None, None, 1, 0, 8) == sw.SWIGLU_OK
 
 
-def fc1(lib, a, lda, w, ldw, y, ldy, x, ldx, m, n, k, dt=BF16):
-    return lib.swiglu_fc1_fwd(a, lda, w, ldw, y, ldy, x, ldx, m, n, k, dt, None)
+def fc1(lib, a, lda, w, ldw, y, ldy, x, ldx, m, n, k, dt=BF16, ws=None):
+    return lib.swiglu_fc1_fwd(a, lda, w, ldw, y, ldy, x, ldx, m, n, k, dt, ws, None)
 
 
 @no_gpu_only
@@ -296,7 +296,8 @@ def test_fc1_validation(lib):
     def call(**kw):
         args = {**ok, **kw}
         return fc1(lib, args["a"], args["lda"], args["w"], args["ldw"], args["y"], args["ldy"],
-                   args["x"], args["ldx"], args["m"], args["n"], args["k"], kw.get("dt", BF16))
+                   args["x"], args["ldx"], args["m"], args["n"], args["k"], kw.get("dt", BF16),
+                   kw.get("ws"))
 
     assert call(dt=F32) == sw.SWIGLU_ERR_BAD_DTYPE
     # shapes: n and k multiples of 64, n <= 2^30, nothing negative
@@ -331,6 +332,13 @@ def test_fc1_validation(lib):
     assert call(x=A, ldx=256) == sw.SWIGLU_ERR_ALIASING
     assert call(x=B + 4096, ldx=256) == sw.SWIGLU_ERR_ALIASING
     assert call(x=C + 512, ldx=256) == sw.SWIGLU_ERR_ALIASING
+    # the tile-queue workspace: 16-byte aligned, apart from every operand
+    assert lib.swiglu_fc1_workspace_size() == 9 * 128
+    assert call(ws=D + 8) == sw.SWIGLU_ERR_BAD_STRIDE
+    assert call(ws=A + 256) == sw.SWIGLU_ERR_ALIASING
+    assert call(ws=B - 1024) == sw.SWIGLU_ERR_ALIASING               # its 1152 bytes reach w
+    assert call(ws=C + 512) == sw.SWIGLU_ERR_ALIASING
+    assert call(x=D, ldx=256, ws=D + 1024) == sw.SWIGLU_ERR_ALIASING
 
 
 @no_gpu_only

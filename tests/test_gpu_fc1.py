@@ -132,8 +132,9 @@ def test_fc1_full_size_sampled(hidden, n):
     w = (torch.randn(2 * n, hidden, device="cuda", generator=gen) / hidden ** 0.5).bfloat16()
     y = sw.swiglu_fc1_fwd(a, w)
     y2, x = sw.swiglu_fc1_fwd(a, w, x_out=True)
+    y3 = sw.swiglu_fc1_fwd(a, w, workspace=False)      # one workgroup per tile
     torch.cuda.synchronize()
-    assert gu.bits_equal(y, y2)
+    assert gu.bits_equal(y, y2) and gu.bits_equal(y, y3)
     rng = np.random.default_rng(hidden + n)
     toks = np.unique(np.concatenate([[0, 1, 255, 256, 511, m - 1],
                                      rng.choice(m, 58, replace=False)]))
@@ -146,7 +147,62 @@ def test_fc1_full_size_sampled(hidden, n):
     y_s = y[ti][:, fi]
     x_s = torch.cat([x[ti][:, fi], x[ti][:, fi + n]], dim=1)
     _check(a_s, w_s, y_s, x_s)
-    del a, w, y, y2, x
+    del a, w, y, y2, y3, x
+
+
+@pytest.mark.parametrize("m", [8192, 8192 + 100])
+def test_fc1_tile_pool(m):
+    """A launch of at least 16 tiles per CU (128 feature tiles x 32 or 33
+    token tiles) ends on a pool of tiles that workgroups take through the
+    workspace's queues. Three calls in a row on one workspace: y and the
+    product are the same bits as with one workgroup per tile, the workspace
+    is all zero after each call, and y matches the oracle on sampled pairs
+    from the pool's tiles (the last quarter of the launch order: features
+    12288 and up) and from the fixed ones."""
+    n, k = 16384, 128
+    print(f"[fc1 pool] m={m} n={n} k={k}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(m)
+    a = torch.randn(m, k, device="cuda", generator=gen).bfloat16()
+    w = (torch.randn(2 * n, k, device="cuda", generator=gen) / k ** 0.5).bfloat16()
+    y_fixed, x_fixed = sw.swiglu_fc1_fwd(a, w, x_out=True, workspace=False)
+    ws = torch.zeros(sw.swiglu_fc1_workspace_size(), dtype=torch.uint8, device="cuda")
+    for call in range(3):
+        y, x = sw.swiglu_fc1_fwd(a, w, x_out=True, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"    call {call}", flush=True)
+        assert gu.bits_equal(y, y_fixed) and gu.bits_equal(x, x_fixed)
+        assert int(ws.count_nonzero()) == 0
+    rng = np.random.default_rng(m)
+    toks = np.unique(np.concatenate([[0, 255, 256, m - 1], rng.choice(m, 28, replace=False)]))
+    feats = np.unique(np.concatenate([[0, 12287, 12288, n - 1],
+                                      rng.choice(n, 28, replace=False)]))
+    ti = torch.from_numpy(toks).cuda()
+    fi = torch.from_numpy(feats).cuda()
+    _check(gu.from_dev(a[ti]), gu.from_dev(torch.cat([w[fi], w[fi + n]])), y[ti][:, fi])
+
+
+def test_fc1_two_streams():
+    """Launches on two streams at once, each with the binding's own
+    workspace for its stream: both equal the launch with one workgroup per
+    tile."""
+    m, n, k = 8192, 16384, 64
+    print(f"[fc1 streams] m={m} n={n} k={k}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn(m, k, device="cuda", generator=gen).bfloat16()
+    w = (torch.randn(2 * n, k, device="cuda", generator=gen) / k ** 0.5).bfloat16()
+    y_fixed = sw.swiglu_fc1_fwd(a, w, workspace=False)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ys = []
+    for rep in range(2):
+        with torch.cuda.stream(s1):
+            y1 = sw.swiglu_fc1_fwd(a, w)
+        with torch.cuda.stream(s2):
+            y2 = sw.swiglu_fc1_fwd(a, w)
+        ys += [y1, y2]
+    torch.cuda.synchronize()
+    for y in ys:
+        assert gu.bits_equal(y, y_fixed)
 
 
 def test_fc1_strided_operands():

@@ -57,6 +57,11 @@ int main() {
             long long n, tf, tt, maxt, threads;
             std::scanf("%lld %lld %lld %lld %lld", &n, &tf, &tt, &maxt, &threads);
             std::printf("%lld\n", (long long)fc1_rows_per_launch(n, tf, tt, maxt, threads));
+        } else if (op == 'P') {
+            unsigned tiles; long long cus, threads;
+            std::scanf("%u %lld %lld", &tiles, &cus, &threads);
+            Fc1Pool q = fc1_pool(tiles, cus, threads);
+            std::printf("%u %u\n", q.n_fixed, q.grid);
         }
     }
     return 0;
@@ -245,3 +250,32 @@ def test_fc1_launch_chunks(driver, threads):
     # at the default 256 threads every n up to 2^30 gets at least one tile
     if threads == 256:
         assert all(int(line) > 0 for line in got)
+
+
+def test_fc1_pool(driver):
+    """fc1's tile pool: none without a workspace or below 16 tiles per CU;
+    otherwise the fixed tiles are a multiple of 8, about three quarters of
+    the launch, the pool workgroups are at least as many as the pool tiles
+    (every tile is taken), and the grid stays below 2^32 work-items."""
+    rng = np.random.default_rng(11)
+    tiles = sorted({1, 7, 8, 4095, 4096, 4097, 8192, 8193, 65535, 1 << 20, (1 << 24) - 1}
+                   | {int(t) for t in rng.integers(1, 1 << 24, 60)})
+    # (a launch never holds more tiles than fit below 2^32 work-items)
+    cases = [(t, c, th) for t in tiles for c in (0, 32, 256) for th in (256, 512)
+             if t * th < (1 << 32)]
+    got = driver([f"P {t} {c} {th}" for t, c, th in cases])
+    for (t, c, th), line in zip(cases, got):
+        n_fixed, grid = map(int, line.split())
+        if c == 0 or t < 16 * c:
+            assert (n_fixed, grid) == (t, t), (t, c)
+            continue
+        assert grid * th < (1 << 32), (t, c, th)
+        if grid == t:                       # no room for a surplus: no pool
+            assert n_fixed == t
+            continue
+        assert n_fixed % 8 == 0 and n_fixed < t, (t, c)
+        pool = t - n_fixed
+        assert abs(pool - t / 4) <= 16, (t, pool)
+        assert grid - n_fixed > pool, (t, c, th)
+        if t * th * 5 // 4 + 4096 * th < (1 << 32):
+            assert grid - n_fixed >= pool + pool // 4, (t, c)
