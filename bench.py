@@ -237,7 +237,6 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
     """fc1 projection with the SwiGLU epilogue (one kernel) against
     torch.matmul (hipBLASLt) followed by the elementwise SwiGLU, for
     (hidden, n) pairs at the given token count; 2 m k 2n FLOPs."""
-    import numpy as np
     import torch
 
     import swiglu_activation_amd as sw
@@ -250,19 +249,6 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
         xbuf = torch.empty(tokens, 2 * n, dtype=torch.bfloat16, device=dev)
         flops = 2.0 * tokens * hidden * 2 * n
 
-        def timed(fn, warmup=20):
-            # back to back on the stream, one synchronisation at the end (so
-            # the GPU never idles between launches); mean of the timed ones
-            ev = []
-            for k in range(iters + warmup):
-                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s0.record(stream)
-                fn()
-                s1.record(stream)
-                ev.append((s0, s1))
-            ev[-1][1].synchronize()
-            return float(np.mean([a.elapsed_time(b) for a, b in ev[warmup:]]))
-
         if si == 0:
             # Untimed: sustained matrix-core load until the clocks have
             # settled (a few launches are not enough; the first ~100 ms of
@@ -272,10 +258,14 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
                 for _ in range(8):
                     sw.swiglu_fc1_fwd(a, wt, y)
                 torch.cuda.synchronize()
-        fused = timed(lambda: sw.swiglu_fc1_fwd(a, wt, y))
-        fused_x = timed(lambda: sw.swiglu_fc1_fwd(a, wt, y, x_out=xbuf))
-        mm = timed(lambda: torch.matmul(a, wt.t(), out=xbuf))
-        unfused = timed(lambda: (torch.matmul(a, wt.t(), out=xbuf), sw.swiglu_gateup_fwd(xbuf, y)))
+        # Each comparison alternates its two sides launch by launch, so both
+        # see the same clocks (which drift by several percent over seconds
+        # of matrix-core load); medians over the pairs.
+        fused, unfused = pair_times(
+            stream, lambda: sw.swiglu_fc1_fwd(a, wt, y),
+            lambda: (torch.matmul(a, wt.t(), out=xbuf), sw.swiglu_gateup_fwd(xbuf, y)), iters)
+        fused_x, mm = pair_times(stream, lambda: sw.swiglu_fc1_fwd(a, wt, y, x_out=xbuf),
+                                 lambda: torch.matmul(a, wt.t(), out=xbuf), iters)
         out[f"tokens{tokens}_hidden{hidden}_n{n}"] = {
             "roofline": {"bound": "mfma", "kernel": "swiglu_fc1_kernel",
                          "achieved": round(flops / fused / 1e9, 1), "peak": PEAK_BF16_TFLOPS,

@@ -126,12 +126,15 @@ struct Fc1Pool {
     uint32_t n_fixed, grid;
 };
 
-inline Fc1Pool fc1_pool(uint32_t tiles, int64_t cus, int64_t threads) {
+inline Fc1Pool fc1_pool(uint32_t tiles, int64_t cus, int64_t threads, uint32_t pool_div = 4,
+                        uint32_t surplus_div = 4) {
     if (cus <= 0 || (int64_t)tiles < 16 * cus) return {tiles, tiles};
-    const uint32_t n_fixed = tiles / 8 * 8 - tiles / 4 / 8 * 8;   // about three quarters
+    // (pool_div, surplus_div: the pool is 1 / pool_div of the launch, and
+    // the pool workgroups 1 + 1 / surplus_div times its tiles)
+    const uint32_t n_fixed = tiles / 8 * 8 - tiles / pool_div / 8 * 8;
     const uint32_t pool = tiles - n_fixed;
     const int64_t max_wg = (((int64_t)1 << 32) - 1) / threads;
-    int64_t grid = (int64_t)tiles + (pool + 3) / 4;
+    int64_t grid = (int64_t)tiles + (pool + surplus_div - 1) / surplus_div;
     if (grid > max_wg) grid = max_wg;
     if (grid <= (int64_t)tiles) return {tiles, tiles};
     return {n_fixed, (uint32_t)grid};

@@ -62,6 +62,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef SWIGLU_FC_XCD
 #define SWIGLU_FC_XCD 0         // give each XCD a contiguous range of the launch order
 #endif
+#ifndef SWIGLU_FC_POOL_DIV
+#define SWIGLU_FC_POOL_DIV 4    // with a workspace: the last 1 / POOL_DIV of a large launch is a pool
+#endif
+#ifndef SWIGLU_FC_SURPLUS_DIV
+#define SWIGLU_FC_SURPLUS_DIV 4 // ... taken by 1 + 1 / SURPLUS_DIV times as many workgroups
+#endif
 #ifndef SWIGLU_FC_LDS_EPI
 #define SWIGLU_FC_LDS_EPI 1     // stage the epilogue through LDS for whole-line stores
 #endif
@@ -983,7 +989,7 @@ __attribute__((visibility("default"))) swiglu_status swiglu_fc1_fwd(
         P.m = mc;
         t_tiles = (uint32_t)((mc + kFcTileT - 1) / kFcTileT);
         const uint32_t tiles = f_tiles * t_tiles;
-        const swiglu_host::Fc1Pool pool = swiglu_host::fc1_pool(tiles, cus, kFcThreads);
+        const swiglu_host::Fc1Pool pool = swiglu_host::fc1_pool(tiles, cus, kFcThreads, SWIGLU_FC_POOL_DIV, SWIGLU_FC_SURPLUS_DIV);
         n_fixed = pool.n_fixed;
         const uint32_t grid = pool.grid;
         if (hipLaunchKernel(reinterpret_cast<const void*>(&swiglu_fc1_kernel), dim3(grid),
