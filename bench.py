@@ -194,13 +194,20 @@ def cpu_baseline_other_rows(w, x_h, dy_h, rows: int = 512):
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 
 
-def pair_times(stream, f1, f2, iters: int, warm_s: float = 0.1):
-    """Median event times (ms) of f1 and of f2, run alternately back to back
+def pair_times(stream, f1, f2, iters: int, warm_s: float = 0.1, between=None):
+    """Medians of pair_samples (ms)."""
+    import numpy as np
+    t1, t2 = pair_samples(stream, f1, f2, iters, warm_s, between)
+    return float(np.median(t1)), float(np.median(t2))
+
+
+def pair_samples(stream, f1, f2, iters: int, warm_s: float = 0.1, between=None):
+    """Event times (ms) of f1 and of f2, pair by pair, run alternately back to back
     on `stream`: untimed pairs for `warm_s` seconds first (the first few
     milliseconds of a new load can run up to 15 % slow while the clocks
     settle), then `iters` timed pairs with one synchronisation at the end, so
-    the GPU never idles between launches."""
-    import numpy as np
+    the GPU never idles between launches. `between` (untimed) runs before
+    each timed call, e.g. to leave the caches in the same state for both."""
     import torch
     t_end = time.perf_counter() + warm_s
     while True:
@@ -212,16 +219,21 @@ def pair_times(stream, f1, f2, iters: int, warm_s: float = 0.1):
             break
     ev = []
     for _ in range(iters):
-        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a, b, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+        if between is not None:
+            between()
         a.record(stream)
         f1()
         b.record(stream)
-        f2()
+        if between is not None:
+            between()
         c.record(stream)
-        ev.append((a, b, c))
-    ev[-1][2].synchronize()
-    t = [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev]
-    return float(np.median([x[0] for x in t])), float(np.median([x[1] for x in t]))
+        f2()
+        d.record(stream)
+        ev.append((a, b, c, d))
+    ev[-1][3].synchronize()
+    t = [(a.elapsed_time(b), c.elapsed_time(d)) for a, b, c, d in ev]
+    return [x[0] for x in t], [x[1] for x in t]
 
 
 def hbm_roofline(kernel: str, bytes_: float, ms: float) -> dict:
@@ -232,11 +244,12 @@ def hbm_roofline(kernel: str, bytes_: float, ms: float) -> dict:
             "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "bytes_per_launch": bytes_}
 
 
-def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iters: int = 10,
+def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iters: int = 25,
             clock_warmup_s: float = 0.3):
     """fc1 projection with the SwiGLU epilogue (one kernel) against
     torch.matmul (hipBLASLt) followed by the elementwise SwiGLU, for
     (hidden, n) pairs at the given token count; 2 m k 2n FLOPs."""
+    import numpy as np
     import torch
 
     import swiglu_activation_amd as sw
@@ -260,12 +273,26 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
                 torch.cuda.synchronize()
         # Each comparison alternates its two sides launch by launch, so both
         # see the same clocks (which drift by several percent over seconds
-        # of matrix-core load); medians over the pairs.
-        fused, unfused = pair_times(
+        # of matrix-core load); medians over the pairs. Before each timed
+        # launch, 512 MiB are written (untimed), which evicts the 256 MiB
+        # Infinity Cache: both sides start with their inputs in HBM, as after
+        # the other layers of a model, instead of one side finding what the
+        # other left behind.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = flush.zero_
+        tf, tu = pair_samples(
             stream, lambda: sw.swiglu_fc1_fwd(a, wt, y),
-            lambda: (torch.matmul(a, wt.t(), out=xbuf), sw.swiglu_gateup_fwd(xbuf, y)), iters)
-        fused_x, mm = pair_times(stream, lambda: sw.swiglu_fc1_fwd(a, wt, y, x_out=xbuf),
-                                 lambda: torch.matmul(a, wt.t(), out=xbuf), iters)
+            lambda: (torch.matmul(a, wt.t(), out=xbuf), sw.swiglu_gateup_fwd(xbuf, y)), iters,
+            between=cold)
+        tfx, tm = pair_samples(stream, lambda: sw.swiglu_fc1_fwd(a, wt, y, x_out=xbuf),
+                               lambda: torch.matmul(a, wt.t(), out=xbuf), iters, between=cold)
+        del flush
+        med = lambda v: float(np.median(v))
+        fused, unfused, fused_x, mm = med(tf), med(tu), med(tfx), med(tm)
+        # the clocks move by up to 30 % over tens of milliseconds: the ratio
+        # within each pair is the steadier comparison
+        ratio = med([f / u for f, u in zip(tf, tu)])
+        ratio_x = med([f / u for f, u in zip(tfx, tm)])
         out[f"tokens{tokens}_hidden{hidden}_n{n}"] = {
             "roofline": {"bound": "mfma", "kernel": "swiglu_fc1_kernel",
                          "achieved": round(flops / fused / 1e9, 1), "peak": PEAK_BF16_TFLOPS,
@@ -276,7 +303,10 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
             "fused_with_x_ms": round(fused_x, 4),
             "hipblaslt_matmul_ms": round(mm, 4),
             "hipblaslt_TFLOPs": round(flops / mm / 1e9, 1),
-            "matmul_then_swiglu_ms": round(unfused, 4)}
+            "matmul_then_swiglu_ms": round(unfused, 4),
+            "fused_over_matmul_then_swiglu": round(ratio, 4),
+            "fused_with_x_over_matmul": round(ratio_x, 4),
+            "pairs": iters}
         log(f"[bench] fc1 h={hidden} n={n}: fused {fused:.3f} ms ({flops / fused / 1e9:.0f} TFLOP/s), "
             f"matmul {mm:.3f} ms, matmul+swiglu {unfused:.3f} ms")
         del a, wt, y, xbuf
