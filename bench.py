@@ -289,6 +289,21 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
         del flush
         med = lambda v: float(np.median(v))
         fused, unfused, fused_x, mm = med(tf), med(tu), med(tfx), med(tm)
+
+        def warm(fn, reps=10):
+            # back to back with itself, so its inputs stay in the caches
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        fused_warm = warm(lambda: sw.swiglu_fc1_fwd(a, wt, y))
+        unfused_warm = warm(lambda: (torch.matmul(a, wt.t(), out=xbuf), sw.swiglu_gateup_fwd(xbuf, y)))
         # the clocks move by up to 30 % over tens of milliseconds: the ratio
         # within each pair is the steadier comparison
         ratio = med([f / u for f, u in zip(tf, tu)])
@@ -305,10 +320,13 @@ def fc1_leg(dev, stream, tokens: int, shapes=((4096, 4096), (8192, 32768)), iter
             "hipblaslt_TFLOPs": round(flops / mm / 1e9, 1),
             "matmul_then_swiglu_ms": round(unfused, 4),
             "fused_over_matmul_then_swiglu": round(ratio, 4),
+            "warm": {"fused_ms": round(fused_warm, 4), "matmul_then_swiglu_ms": round(unfused_warm, 4),
+                     "note": "each launched back to back with itself, inputs left in the caches"},
             "fused_with_x_over_matmul": round(ratio_x, 4),
             "pairs": iters}
         log(f"[bench] fc1 h={hidden} n={n}: fused {fused:.3f} ms ({flops / fused / 1e9:.0f} TFLOP/s), "
-            f"matmul {mm:.3f} ms, matmul+swiglu {unfused:.3f} ms")
+            f"matmul {mm:.3f} ms, matmul+swiglu {unfused:.3f} ms (per-pair ratio {ratio:.3f}); "
+            f"warm: fused {fused_warm:.3f} ms, matmul+swiglu {unfused_warm:.3f} ms")
         del a, wt, y, xbuf
     return out
 
