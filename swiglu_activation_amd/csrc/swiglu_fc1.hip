@@ -11,7 +11,8 @@
 //    vector per lane. The roles are swapped relative to y: the MFMA's row
 //    operand is a weight row (an output feature) and its column operand a
 //    token, so each lane ends up holding four consecutive features of one
-//    token and writes y with 8-byte stores.
+//    token. The epilogue passes each wave's tile through LDS (free once the
+//    k loop ends), so every store instruction writes whole 128-byte rows.
 //  * A workgroup of 4 waves computes 256 tokens x 128 features of y; each
 //    wave 128 tokens x 64 features, i.e. 4 x 2 MFMA tiles for the gate and
 //    4 x 2 for the up projection (256 fp32 accumulators per lane, in the
@@ -39,13 +40,18 @@
 //    (half of the next slot's token copies in step 0, the weight copies in
 //    steps 1 and 2, half of the token copies after the barrier), not issued
 //    in a burst: a burst fills the copy queue, and the wave, which issues in
-//    order, then stalls in front of its next MFMA.
+//    order, then stalls in front of its next MFMA. Each step is written out
+//    as its 16 MFMAs with the fragment reads and copies pinned after chosen
+//    ones (scheduling barriers), so the compiler cannot bunch them.
 //    Each copy is addressed as a wave-uniform base in scalar registers plus
 //    a fixed 32-bit lane offset, so no vector instruction sits between two
 //    copies (which limits lda and ldw to 2^28 elements).
 //  * Rows past m (tokens) or n (features) are clamped to the last valid row:
 //    they copy real data, which reaches only accumulators that are never
 //    stored.
+//  * With a workspace, the last quarter of a large launch's tiles is a pool
+//    taken through per-XCD queues, so XCDs running at higher clocks take
+//    more tiles instead of idling at the end (below, at the kernel).
 #include "swiglu_device.h"
 
 namespace {
