@@ -28,8 +28,8 @@ as Fc1SwiGLU. Its forward either runs the projection as a library GEMM
 product (the default), or, with fused_epilogue=True, the one kernel that
 computes the projection with the SwiGLU as its epilogue and also writes the
 product. The default is the faster of the two on MI355X: with the product
-written (as the backward needs it), the GEMM then the SwiGLU took 5.83 ms
-against 6.08 ms for the fused kernel at 8192 tokens, hidden 8192 and
+written (as the backward needs it), the GEMM then the SwiGLU took 5.92 ms
+against 6.11 ms for the fused kernel at 8192 tokens, hidden 8192 and
 n = 32768, and the two were level at hidden 4096, n = 4096. The backward is
 the SwiGLU backward kernel followed by the two weight and input GEMMs of
 the projection (plain library GEMMs through torch.matmul).

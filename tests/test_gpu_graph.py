@@ -104,3 +104,30 @@ def test_fc1_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert gu.bits_equal(y_s, y_e), r
+
+
+def test_fc1_pool_with_explicit_workspace_replays_match_eager():
+    """A launch large enough for the tile pool (128 feature tiles x 32 token
+    tiles), captured with a caller's workspace: the last pool workgroup
+    clears the queue counters inside every replay, so each replay matches
+    an eager call with no workspace, and the workspace is zero after each."""
+    m, n, k = 8192, 16384, 64
+    print(f"[graph] fc1 pool m {m} n {n} k {k}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(63)
+    a_s = torch.randn(m, k, device="cuda", generator=gen).bfloat16()
+    w_s = (torch.randn(2 * n, k, device="cuda", generator=gen) / k ** 0.5).bfloat16()
+    y_s = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(sw.swiglu_fc1_workspace_size(), dtype=torch.uint8, device="cuda")
+    sw.swiglu_fc1_fwd(a_s, w_s, y_s, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sw.swiglu_fc1_fwd(a_s, w_s, y_s, workspace=ws)
+    for r in range(REPLAYS):
+        a_s.copy_(torch.randn(m, k, device="cuda", generator=gen).bfloat16())
+        y_e = sw.swiglu_fc1_fwd(a_s, w_s, workspace=False)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert gu.bits_equal(y_s, y_e), r
+        assert int(ws.count_nonzero()) == 0, r
