@@ -60,10 +60,16 @@ def _check(a_h, w_h, y, x=None):
 
 
 @pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 256, 512), (300, 192, 320),
-                                   (1, 64, 64), (1000, 1792, 1024), (4096, 512, 4096)])
+                                   (1, 64, 64), (1000, 1792, 1024), (4096, 512, 4096),
+                                   (260, 320, 384), (192, 128, 192), (96, 64, 1984),
+                                   (64, 128, 65536)])
 def test_fc1_swiglu_parity(m, n, k):
-    """Ragged token counts (300, 1, 1000), a feature count that leaves a
-    half-empty 128-wide tile (192, 1792), and long k."""
+    """Ragged token counts (300, 1, 1000, 260), a feature count that leaves a
+    half-empty 128-wide tile (192, 1792, 320), and long k (up to 65536). The
+    k loop is unrolled over periods of 6 k tiles and skips the first
+    (-k/64) mod 6 slots; these k cover every count of skipped slots: 64 and
+    1984 skip 5, 512 skips 4, 192 skips 3, 1024, 4096 and 65536 skip 2, 320
+    skips 1, 384 skips none."""
     print(f"[fc1] m={m} n={n} k={k}", flush=True)
     a_h, w_h = _case(m, n, k, seed=m + n + k)
     a, w = gu.to_dev(a_h, "bf16"), gu.to_dev(w_h, "bf16")
@@ -224,3 +230,31 @@ def test_fc1_strided_operands():
     y_dense = sw.swiglu_fc1_fwd(gu.to_dev(a_h, "bf16"), gu.to_dev(w_h, "bf16"))
     torch.cuda.synchronize()
     assert gu.bits_equal(y, y_dense)
+
+
+@pytest.mark.parametrize("m,n,k", [(96, 128, 65536), (300, 192, 2496)])
+def test_fc1_exact_sums(m, n, k):
+    """Inputs chosen so that fp32 accumulation is exact in any order: a in
+    {-1, 0, 1}, w in {-1/8, 0, 1/8}, so every product is a multiple of 1/8
+    and every partial sum stays below 2^24 / 8 in magnitude. A missing,
+    repeated or misplaced k tile then shows as a wrong value, which the
+    fp32-accumulation bound of the other tests (k 2^-24 |A||W|, about 0.4
+    at k = 65536) would not catch. The product must equal the oracle's
+    nearest-even bf16 rounding of the exact sums bit for bit, and y must be
+    within 2 bf16 ulp of the oracle's correctly rounded value.
+    k = 65536 runs 1024 k tiles (two skipped slots); 2496 runs 39 (three)."""
+    print(f"[fc1 exact] m={m} n={n} k={k}", flush=True)
+    rng = np.random.default_rng(m + k)
+    a_h = oracle.round_f64_to_bf16_bits(rng.integers(-1, 2, (m, k)).astype(np.float64))
+    w_h = oracle.round_f64_to_bf16_bits(rng.integers(-1, 2, (2 * n, k)).astype(np.float64) / 8)
+    a, w = gu.to_dev(a_h, "bf16"), gu.to_dev(w_h, "bf16")
+    y, x = sw.swiglu_fc1_fwd(a, w, x_out=True)
+    torch.cuda.synchronize()
+    af, wf = oracle.widen(a_h, "bf16"), oracle.widen(w_h, "bf16")
+    xref = oracle.oracle_fc1(af, wf)
+    assert np.max(np.abs(xref)) * 8 < 2 ** 24            # every partial sum is exact in fp32
+    assert np.array_equal(gu.from_dev(x), oracle.round_f64_to_bf16_bits(xref))
+    yref = oracle.round_f64_to_bf16_bits(oracle.oracle_fwd(xref))
+    dist = oracle.bf16_ulp_distance(gu.from_dev(y), yref)
+    print(f"    y: max {int(dist.max())} ulp over {dist.size}", flush=True)
+    assert int(dist.max()) <= 2
