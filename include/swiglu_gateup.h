@@ -299,14 +299,16 @@ swiglu_status swiglu_gateup_bias_scale_bwd_noalloc(const void* dy, int64_t dy_ro
  *   dtype         must be SWIGLU_DTYPE_BF16.
  *   workspace     NULL, or swiglu_fc1_workspace_size() bytes of device memory,
  *                 owned by the caller, that are all zero on entry. With it,
- *                 the kernel runs one workgroup per CU, and the workgroups
- *                 share the output tiles through counters kept there. Tiles
- *                 then go to whichever XCD is free, instead of a fixed share
- *                 each. The call leaves the workspace all zero again once it
- *                 completes, so one workspace serves every call on one
- *                 stream. Calls that use the same workspace must not overlap
- *                 in time (e.g. on two streams). With NULL, each tile is its
- *                 own workgroup. y and x_out are the same bits either way.
+ *                 a launch of at least 16 output tiles (256 x 128) per CU
+ *                 ends on a pool. Its last quarter of tiles is taken by
+ *                 workgroups as they start, through counters kept there, so
+ *                 those tiles go to whichever XCD has room instead of a
+ *                 fixed share each. The call leaves the workspace all zero
+ *                 again once it completes, so one workspace serves every
+ *                 call on one stream. Calls that use the same workspace must
+ *                 not overlap in time (e.g. on two streams). With NULL, every
+ *                 tile is its own workgroup. y and x_out are the same bits
+ *                 either way.
  *   stream        HIP stream of the launch.
  * All pointers must be 16-byte aligned and all row strides multiples of 8;
  * lda and ldw (hence k) are at most 2^28 elements.
