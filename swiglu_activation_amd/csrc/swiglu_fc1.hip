@@ -469,7 +469,11 @@ __device__ __forceinline__ void epi_out(uint16_t* region, int64_t tw, int64_t fw
         const int row = kRowsPerPass * it + lane / kChunks, col = 8 * (lane % kChunks);
         const u32x4 v = *reinterpret_cast<const u32x4*>(region + row * kEpiPitch + col);
         const int64_t tok = tw + row, f = fw + col;
+#if SWIGLU_FC_NT_EPI
+        if (tok < m && f < n) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + tok * ld + f));
+#else
         if (tok < m && f < n) *reinterpret_cast<u32x4*>(out + tok * ld + f) = v;
+#endif
     }
 }
 
